@@ -1,0 +1,239 @@
+"""Benchmark of the hot path on one MI355X; prints ONE JSON line.
+
+A step is one pass of the whole path on synthetic inputs already resident in
+HBM:
+  * attn_fwd on the headline workload -- one head, Nq = Nk = 4096, D = 64,
+    float32 in and out (the size "Flash attention, f32" benchmarks), and
+  * flash-decoding -- attn_decode_split + attn_decode_combine on batch 8,
+    32 heads, one query row, KV length 32768, D = 128, float16.
+``value`` is the forward's TFLOP/s (4*Nq*Nk*D flops per call); the decode's
+KV GB/s rides along in ``decode``.  Both carry a roofline fraction; the
+kernels' own durations come from HIP events recorded on the stream the
+kernels are launched on, around each part of every timed step.
+
+After the timed region the multi-head f16/bf16 workload (B4 H12 M=N=2048
+D64) and the causal f16 workload (Z1 H2 N1024, scale 0.5, with LSE) are timed
+the same way and reported under ``extra`` (not part of ``value``).
+
+The fp64 CPU oracle is timed on the host cores first (``cpu_baseline``): the
+full headline workload, all 4096 rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F32 = 157.3          # TFLOP/s, MI355X dense f32 matrix (= f32 vector)
+PEAK_F16 = 2516.6         # TFLOP/s, MI355X dense f16/bf16 matrix
+PEAK_HBM = 8000.0         # GB/s
+PAGES_F32_TFLOPS = 5.5    # "Flash attention, f32": same workload, RTX 2080 SUPER (context)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg):
+    import oracle
+    from exact_attention_fa2_amd import inputs
+    q, k, v = inputs.qkv((cfg.B, cfg.H, cfg.Nq, cfg.D), (cfg.B, cfg.H, cfg.Nk, cfg.D), cfg.seed,
+                         cfg.dtype)
+    q, k, v = (inputs.to_f64(x, cfg.dtype) for x in (q, k, v))
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.attn(q, k, v, cfg.scale, cfg.causal, nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": cfg.flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "%s, all %d rows, fp64, %.2f s wall" % (cfg.name, cfg.B * cfg.H * cfg.Nq, dt)}
+
+
+def upload(a, dt):
+    import numpy as np
+    import torch
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def prefill_inputs(cfg):
+    from exact_attention_fa2_amd import inputs
+    q, k, v = inputs.qkv((cfg.B, cfg.H, cfg.Nq, cfg.D), (cfg.B, cfg.H, cfg.Nk, cfg.D), cfg.seed,
+                         cfg.dtype)
+    return [upload(x, cfg.dtype) for x in (q, k, v)]
+
+
+def decode_inputs(cfg):
+    from exact_attention_fa2_amd import inputs
+    out = []
+    for tid, shape in ((0, (cfg.B, cfg.H, cfg.D)), (1, (cfg.B, cfg.H, cfg.N, cfg.D)),
+                       (2, (cfg.B, cfg.H, cfg.N, cfg.D))):
+        a = inputs.normal(shape, cfg.seed, tid, cfg.dtype)
+        out.append(upload(a, cfg.dtype))
+        del a
+    return out
+
+
+def time_loop(fn, iters, warmup):
+    """Mean kernel time (ms) of fn() over iters calls, events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=25)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--decode-dtype", default="f16", choices=["f16", "bf16"])
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path has no multi-GPU form "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    from exact_attention_fa2_amd import fa2, workloads
+    pre = workloads.HEADLINE_F32
+    dec = workloads.decode(args.decode_dtype)
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on %s" % pre.name)
+        base = cpu_baseline(pre)
+        log("cpu baseline: %.4f TFLOP/s on %d cores" % (base["value"], base["cores"]))
+
+    import torch
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log("device: %s, %d CUs" % (props.name, props.multi_processor_count))
+
+    pq, pk, pv = prefill_inputs(pre)
+    po = torch.empty_like(pq)
+    log("decode inputs: generating %s" % dec.name)
+    dq, dk, dv = decode_inputs(dec)
+    ns = fa2.default_splits(dec.B, dec.H, dec.N, dec.D)
+    op = torch.empty((dec.B, dec.H, ns, dec.D), dtype=torch.float32, device="cuda")
+    mp = torch.empty((dec.B, dec.H, ns), dtype=torch.float32, device="cuda")
+    lp = torch.empty((dec.B, dec.H, ns), dtype=torch.float32, device="cuda")
+    do = torch.empty((dec.B, dec.H, dec.D), dtype=dq.dtype, device="cuda")
+
+    def prefill():
+        fa2.attn_fwd(pq, pk, pv, scale=pre.scale, out=po)
+
+    def split():
+        fa2.attn_decode_split(dq, dk, dv, dec.scale, ns, op, mp, lp)
+
+    def combine():
+        fa2.attn_decode_combine(op, mp, lp, dq.dtype, out=do)
+
+    for _ in range(args.warmup):
+        prefill()
+        split()
+        combine()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        ev[i][0].record()
+        prefill()
+        ev[i][1].record()
+        split()
+        ev[i][2].record()
+        combine()
+        ev[i][3].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    split_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    comb_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    dec_ms = split_ms + comb_ms
+
+    tflops = pre.flops / (pre_ms * 1e-3) / 1e12
+    dec_gbs = dec.kv_bytes / (dec_ms * 1e-3) / 1e9
+    split_gbs = dec.kv_bytes / (split_ms * 1e-3) / 1e9
+    log("prefill %.2f us (%.2f TFLOP/s)  decode split %.2f us + combine %.2f us (%.1f GB/s)" % (
+        pre_ms * 1e3, tflops, split_ms * 1e3, comb_ms * 1e3, dec_gbs))
+
+    extra = {}
+    if not args.no_extra:
+        del dk, dv
+        torch.cuda.empty_cache()
+        for cfg in (workloads.multihead(2048, "f16"), workloads.multihead(2048, "bf16"),
+                    workloads.causal_lse(True), workloads.causal_lse(False)):
+            q, k, v = prefill_inputs(cfg)
+            o = torch.empty_like(q)
+            lse = torch.empty((cfg.B, cfg.H, cfg.Nq), dtype=torch.float32, device="cuda")
+            ms = time_loop(lambda: fa2.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal,
+                                                out=o, return_lse=True, lse=lse),
+                           max(K, 50), args.warmup)
+            tf = cfg.flops / (ms * 1e-3) / 1e12
+            extra[cfg.name] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 2),
+                               "frac_of_mfma_peak": round(tf / PEAK_F16, 4)}
+            log("%s: %.2f us, %.1f TFLOP/s (%.1f%% of MFMA peak)" % (cfg.name, ms * 1e3, tf,
+                                                                     100 * tf / PEAK_F16))
+            del q, k, v, o, lse
+
+    line = {
+        "metric": "attention fwd TFLOP/s (N=4096,D=64) + decode KV GB/s; % of roofline",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tflops / PAGES_F32_TFLOPS, 3),
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill: %s, scale 1/8, non-causal; decode: %s, n_splits %d" % (
+                pre.name, dec.name, ns),
+            "prefill": {"B": pre.B, "H": pre.H, "Nq": pre.Nq, "Nk": pre.Nk, "D": pre.D,
+                        "dtype": pre.dtype, "causal": pre.causal},
+            "decode": {"B": dec.B, "H": dec.H, "N": dec.N, "D": dec.D, "dtype": dec.dtype,
+                       "n_splits": ns},
+        },
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_F32,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_F32, 4), "traffic": None,
+                     "kernel": "fwd_f32_d64", "us": round(pre_ms * 1e3, 3)},
+        "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "us": round(dec_ms * 1e3, 2),
+                   "split_us": round(split_ms * 1e3, 2), "combine_us": round(comb_ms * 1e3, 2),
+                   "bytes": dec.kv_bytes},
+        "roofline_decode": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": PEAK_HBM,
+                            "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM, 4),
+                            "traffic": None, "kernel": "decode_split",
+                            "us": round(split_ms * 1e3, 2)},
+        "extra": extra,
+        "cpu_baseline": base,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,135 @@
+// api.cpp -- the C ABI declared in include/fa2.h: argument checks, device
+// checks and dispatch to the kernel launchers.  Nothing here allocates,
+// frees or synchronises; every launch goes on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "fa2_internal.h"
+
+#define FA2_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr long long kMaxSliceBytes = (1LL << 31) - (1LL << 20);
+
+struct DeviceInfo {
+    int ok = 0;
+    int num_cus = 0;
+};
+
+std::once_flag g_once[kMaxDevices];
+DeviceInfo g_info[kMaxDevices];
+
+// Properties of the current device, filled once per device (thread-safe).
+const DeviceInfo *current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_once[dev], [dev] {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return;
+        g_info[dev].num_cus = p.multiProcessorCount;
+        g_info[dev].ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    });
+    return g_info[dev].ok ? &g_info[dev] : nullptr;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int esize(fa2_dtype dt) { return dt == FA2_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == FA2_F32 || dt == FA2_F16 || dt == FA2_BF16; }
+
+}  // namespace
+
+FA2_API fa2_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                            fa2_dtype dtype, void *stream) {
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 1 || D < 1) return FA2_ERR_SHAPE;
+    if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return FA2_ERR_UNSUPPORTED;
+    if (D != 64) return FA2_ERR_UNSUPPORTED;
+    if (causal && Nq != Nk) return FA2_ERR_UNSUPPORTED;
+    if ((long long)B * H * Nq == 0) return FA2_OK;  // nothing to compute
+    if (!q || !k || !v || !o) return FA2_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        (lse && ((uintptr_t)lse & 3u)))
+        return FA2_ERR_ALIGN;
+    const long long es = esize(dtype);
+    if ((long long)Nk * D * es > kMaxSliceBytes || (long long)Nq * D * es > kMaxSliceBytes)
+        return FA2_ERR_UNSUPPORTED;
+    if ((long long)B * H > 65535) return FA2_ERR_UNSUPPORTED;
+    const DeviceInfo *dev = current_device();
+    if (!dev) return FA2_ERR_DEVICE;
+    fa2::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, scale, causal, dev->num_cus};
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == FA2_F32) return fa2::launch_fwd_f32_d64(a, st);
+    return fa2::launch_fwd_mfma_d64(a, dtype, st);
+}
+
+FA2_API fa2_status attn_decode_split(const void *q, const void *k, const void *v,
+                                     float *o_part, float *m_part, float *l_part, int B, int H,
+                                     int N, int D, float scale, int n_splits, fa2_dtype dtype,
+                                     void *stream) {
+    if (B < 0 || H < 0 || N < 1 || D < 1 || n_splits < 1) return FA2_ERR_SHAPE;
+    if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return FA2_ERR_UNSUPPORTED;
+    if ((long long)B * H == 0) return FA2_OK;
+    if (!q || !k || !v || !o_part || !m_part || !l_part) return FA2_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part) ||
+        ((uintptr_t)m_part & 3u) || ((uintptr_t)l_part & 3u))
+        return FA2_ERR_ALIGN;
+    if ((long long)N * D * esize(dtype) > kMaxSliceBytes) return FA2_ERR_UNSUPPORTED;
+    if ((long long)B * H > 65535 || n_splits > 0x7FFFFFFF / 2) return FA2_ERR_UNSUPPORTED;
+    if (!current_device()) return FA2_ERR_DEVICE;
+    fa2::DecodeArgs a{q, k, v, o_part, m_part, l_part, B, H, N, D, scale, n_splits};
+    return fa2::launch_decode_split(a, dtype, (hipStream_t)stream);
+}
+
+FA2_API fa2_status attn_decode_combine(const float *o_part, const float *m_part,
+                                       const float *l_part, void *o, int B, int H, int D,
+                                       int n_splits, fa2_dtype dtype, void *stream) {
+    if (B < 0 || H < 0 || D < 1 || n_splits < 1) return FA2_ERR_SHAPE;
+    if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return FA2_ERR_UNSUPPORTED;
+    if ((long long)B * H == 0) return FA2_OK;
+    if (!o_part || !m_part || !l_part || !o) return FA2_ERR_NULL;
+    if (((uintptr_t)o_part & 3u) || ((uintptr_t)m_part & 3u) || ((uintptr_t)l_part & 3u) ||
+        !aligned16(o))
+        return FA2_ERR_ALIGN;
+    if ((long long)B * H > 0x7FFFFFFF) return FA2_ERR_UNSUPPORTED;
+    if (!current_device()) return FA2_ERR_DEVICE;
+    return fa2::launch_decode_combine(o_part, m_part, l_part, o, B, H, D, n_splits, dtype,
+                                      (hipStream_t)stream);
+}
+
+FA2_API int attn_decode_default_splits(int B, int H, int N, int D) {
+    (void)D;
+    if (B < 1 || H < 1 || N < 1) return 1;
+    int cus = 256;
+    if (const DeviceInfo *dev = current_device()) cus = dev->num_cus;
+    const long long bh = (long long)B * H;
+    // Aim for about 8 resident workgroups per compute unit, each with at least
+    // 256 keys, and round to a whole number of splits per (b,h).
+    long long want = (8LL * cus + bh - 1) / bh;
+    const long long max_by_len = (N + 255) / 256;
+    if (want > max_by_len) want = max_by_len;
+    if (want < 1) want = 1;
+    return (int)want;
+}
+
+FA2_API const char *fa2_status_string(fa2_status s) {
+    switch (s) {
+        case FA2_OK: return "ok";
+        case FA2_ERR_NULL: return "null pointer";
+        case FA2_ERR_SHAPE: return "invalid shape";
+        case FA2_ERR_UNSUPPORTED: return "unsupported configuration";
+        case FA2_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case FA2_ERR_LAUNCH: return "kernel launch failed";
+        case FA2_ERR_DEVICE: return "no usable gfx950 device";
+    }
+    return "unknown status";
+}

@@ -1,0 +1,44 @@
+// fa2_internal.h -- launchers shared between the kernel sources and the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include "../../include/fa2.h"
+
+namespace fa2 {
+
+// Launch a kernel with hipLaunchKernel so the runtime's verdict is returned.
+template <typename... KArgs, typename... Args>
+inline fa2_status launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                         Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    void *ptrs[] = {(void *)&args...};
+    hipError_t e = hipLaunchKernel((const void *)kern, grid, block, ptrs, 0, st);
+    return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int B, H, Nq, Nk;
+    float scale;
+    int causal;
+    int num_cus;
+};
+
+fa2_status launch_fwd_f32_d64(const FwdArgs &a, hipStream_t st);
+fa2_status launch_fwd_mfma_d64(const FwdArgs &a, fa2_dtype dt, hipStream_t st);
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    float *o_part, *m_part, *l_part;
+    int B, H, N, D;
+    float scale;
+    int n_splits;
+};
+
+fa2_status launch_decode_split(const DecodeArgs &a, fa2_dtype dt, hipStream_t st);
+fa2_status launch_decode_combine(const float *o_part, const float *m_part, const float *l_part,
+                                 void *o, int B, int H, int D, int n_splits, fa2_dtype dt,
+                                 hipStream_t st);
+
+}  // namespace fa2

@@ -1,0 +1,168 @@
+"""ctypes binding of libfa2.so (include/fa2.h).
+
+Marshalling only: tensors are turned into device pointers and the current
+torch stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa2.so")
+
+FA2_F32, FA2_F16, FA2_BF16 = 0, 1, 2
+STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "unsupported configuration",
+          4: "pointer not 16-byte aligned", 5: "kernel launch failed",
+          6: "no usable gfx950 device"}
+
+EXPORTS = ("attn_fwd", "attn_decode_split", "attn_decode_combine",
+           "attn_decode_default_splits", "fa2_status_string")
+
+_lib = None
+
+
+class FA2Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (fn, STATUS.get(status, "?"), status))
+
+
+def lib():
+    """Load libfa2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfa2.so is not built (%s); run "
+                               "`python -m exact_attention_fa2_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, fp, i, f = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.attn_fwd.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp]
+        L.attn_fwd.restype = i
+        L.attn_decode_split.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, f, i, i, vp]
+        L.attn_decode_split.restype = i
+        L.attn_decode_combine.argtypes = [fp, fp, fp, vp, i, i, i, i, i, vp]
+        L.attn_decode_combine.restype = i
+        L.attn_decode_default_splits.argtypes = [i, i, i, i]
+        L.attn_decode_default_splits.restype = i
+        L.fa2_status_string.argtypes = [i]
+        L.fa2_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: FA2_F32, torch.float16: FA2_F16, torch.bfloat16: FA2_BF16}
+    if t.dtype not in m:
+        raise TypeError("unsupported dtype %s" % t.dtype)
+    return m[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise FA2Error(fn, status)
+
+
+def _contig(t, name):
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def attn_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=None,
+             stream=None):
+    """Exact attention forward.  q [B,H,Nq,D], k/v [B,H,Nk,D] (same dtype).
+
+    Returns o (and lse [B,H,Nq] float32 when ``return_lse``)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _contig(t, name)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, D) or v.shape != (B, H, Nk, D):
+        raise ValueError("k and v must be [B,H,Nk,D] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse if return_lse else None),
+                        B, H, Nq, Nk, D, float(scale), int(bool(causal)), dtype_code(q),
+                        _stream(stream))
+    _check("attn_fwd", st)
+    return (out, lse) if return_lse else out
+
+
+def attn_decode_split(q, k, v, scale, n_splits, o_part=None, m_part=None, l_part=None,
+                      stream=None):
+    """Flash-decoding partials.  q [B,H,D], k/v [B,H,N,D]."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _contig(t, name)
+    B, H, D = q.shape
+    N = k.shape[2]
+    if k.shape != (B, H, N, D) or v.shape != (B, H, N, D):
+        raise ValueError("k and v must be [B,H,N,D] matching q")
+    if o_part is None:
+        o_part = torch.empty((B, H, n_splits, D), dtype=torch.float32, device=q.device)
+    if m_part is None:
+        m_part = torch.empty((B, H, n_splits), dtype=torch.float32, device=q.device)
+    if l_part is None:
+        l_part = torch.empty((B, H, n_splits), dtype=torch.float32, device=q.device)
+    st = lib().attn_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(m_part),
+                                 _ptr(l_part), B, H, N, D, float(scale), int(n_splits),
+                                 dtype_code(q), _stream(stream))
+    _check("attn_decode_split", st)
+    return o_part, m_part, l_part
+
+
+def attn_decode_combine(o_part, m_part, l_part, dtype, out=None, stream=None):
+    """Merge partials into o [B,H,D] of ``dtype``."""
+    torch = _torch()
+    B, H, S, D = o_part.shape
+    if out is None:
+        out = torch.empty((B, H, D), dtype=dtype, device=o_part.device)
+    st = lib().attn_decode_combine(_ptr(o_part), _ptr(m_part), _ptr(l_part), _ptr(out), B, H,
+                                   D, S, dtype_code(out), _stream(stream))
+    _check("attn_decode_combine", st)
+    return out
+
+
+def default_splits(B, H, N, D) -> int:
+    return int(lib().attn_decode_default_splits(B, H, N, D))
+
+
+def attn_decode(q, k, v, scale=None, n_splits=None, stream=None):
+    """Split + combine.  q [B,H,D], k/v [B,H,N,D]; returns o [B,H,D]."""
+    B, H, D = q.shape
+    N = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if n_splits is None:
+        n_splits = default_splits(B, H, N, D)
+    parts = attn_decode_split(q, k, v, scale, n_splits, stream=stream)
+    return attn_decode_combine(*parts, dtype=q.dtype, stream=stream)
+
+
+def status_string(code: int) -> str:
+    return lib().fa2_status_string(int(code)).decode()

@@ -1,0 +1,137 @@
+/*
+ * fa2.h -- C ABI of libfa2.so: exact attention forward (FlashAttention-2
+ * schedule) and flash-decoding on AMD Instinct MI355X (gfx950).
+ *
+ * Callers need no HIP header: device pointers are plain `void*`, the stream
+ * is an opaque `void*` holding a hipStream_t (NULL = the default stream).
+ *
+ * Conventions for every entry point
+ *   Ownership  The caller allocates, owns and frees every buffer (device
+ *              memory).  The library never allocates, frees or synchronises;
+ *              its only global state is a once-filled, thread-safe cache of
+ *              device properties.
+ *   Launch     Work is enqueued on `stream` and the call returns at once.
+ *              Results are valid after the stream is synchronised.  Calls on
+ *              one stream run in order; the library keeps no state between
+ *              calls, so calls on different streams may overlap when their
+ *              output buffers do not.
+ *   Layouts    Contiguous row-major, innermost dimension last.  Element type
+ *              of q/k/v/o is `dtype`; lse and decode partials are float32.
+ *   Alignment  Every pointer must be 16-byte aligned (128-bit loads/stores).
+ *   Errors     Arguments are checked before anything is enqueued; a rejected
+ *              call enqueues nothing.  A failed launch is reported as
+ *              FA2_ERR_LAUNCH.  The library never aborts the process.
+ *   Limits     One (b,h) slice of k or v must be smaller than 2 GiB.
+ */
+#ifndef FA2_H
+#define FA2_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA2_F32 = 0,  /* IEEE binary32 */
+    FA2_F16 = 1,  /* IEEE binary16 */
+    FA2_BF16 = 2  /* bfloat16 */
+} fa2_dtype;
+
+typedef enum {
+    FA2_OK = 0,
+    FA2_ERR_NULL = 1,        /* a required pointer is NULL */
+    FA2_ERR_SHAPE = 2,       /* a size is negative or zero where it must be positive */
+    FA2_ERR_UNSUPPORTED = 3, /* valid request this build does not implement (D, dtype,
+                                causal with Nq != Nk, slice >= 2 GiB) */
+    FA2_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    FA2_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch */
+    FA2_ERR_DEVICE = 6       /* no usable gfx950 device, or a device query failed */
+} fa2_status;
+
+/*
+ * attn_fwd -- exact attention forward for [B,H,N,D] tensors.
+ *
+ * Computes, for every batch b, head h and query row i,
+ *     s_ij   = scale * <q[b,h,i,:], k[b,h,j,:]>           for live keys j
+ *     o[b,h,i,:] = sum_j exp(s_ij - m_i) v[b,h,j,:] / sum_j exp(s_ij - m_i)
+ *     lse[b,h,i] = m_i + ln(sum_j exp(s_ij - m_i)),  m_i = max_j s_ij
+ * ("Flash attention, f32": opening paragraph and section Online softmax;
+ *  "Flash Attention" (aarnphm.xyz): sections Deriving the online softmax and
+ *  FlashAttention 2 -- the log-sum-exp per row; "06: Fused attention":
+ *  attn_fwd, causal masking and the per-row L).  Each workgroup walks K/V in
+ *  blocks with a running max, running denominator and an unnormalised
+ *  accumulator, so the Nq x Nk score matrix is never stored.
+ *
+ *   q    [B,H,Nq,D] dtype      k, v [B,H,Nk,D] dtype      o [B,H,Nq,D] dtype
+ *   lse  [B,H,Nq] float32, natural log of the scaled scores; may be NULL.
+ *   causal  0: every key is live.  1: key j is live for query i only when
+ *           j <= i (top-left aligned); requires Nq == Nk.
+ *   scale   multiplies q.k before the softmax (for example 1/sqrt(D)).
+ *   Arithmetic: float32 softmax state and accumulation.  f16/bf16 inputs run
+ *   both products on MFMA with P rounded to the input dtype; float32 inputs
+ *   run both products on float32 MFMA (no reduced-precision rounding).
+ *   o is rounded to nearest-even into dtype.
+ *   Supported: D == 64; dtype F32, F16, BF16; any B, H, Nq >= 0 (zero-size
+ *   outputs enqueue nothing); Nk >= 1; ragged Nq/Nk are masked in the tail.
+ */
+fa2_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                    fa2_dtype dtype, void *stream);
+
+/*
+ * attn_decode_split -- flash-decoding, phase 1: unnormalised partials.
+ *
+ * One query row per (b,h) attends all N keys of its slice, with the keys cut
+ * into n_splits contiguous splits ("Flash decoding": Overview of the
+ * algorithm, and its split kernel).  Split s covers keys
+ * [s*S, min((s+1)*S, N)) with S = ceil(N / n_splits), and stores
+ *     m_part[b,h,s] = max_j s_j                 (s_j = scale * <q[b,h,:], k[b,h,j,:]>)
+ *     l_part[b,h,s] = sum_j exp(s_j - m_part)
+ *     o_part[b,h,s,:] = sum_j exp(s_j - m_part) v[b,h,j,:]   (not divided by l)
+ * in natural-log units of the scaled scores.  A split with no keys (when
+ * n_splits > N) stores m = -inf, l = 0, o = 0.
+ *
+ *   q [B,H,D] dtype;  k, v [B,H,N,D] dtype
+ *   o_part [B,H,n_splits,D] float32;  m_part, l_part [B,H,n_splits] float32
+ *   Supported: D in {64, 128}; dtype F16, BF16, F32; N >= 1; n_splits >= 1;
+ *   B*H == 0 enqueues nothing.
+ */
+fa2_status attn_decode_split(const void *q, const void *k, const void *v,
+                             float *o_part, float *m_part, float *l_part,
+                             int B, int H, int N, int D, float scale, int n_splits,
+                             fa2_dtype dtype, void *stream);
+
+/*
+ * attn_decode_combine -- flash-decoding, phase 2: merge the partials.
+ *
+ *     m_g = max_s m_s,   l_g = sum_s exp(m_s - m_g) l_s,
+ *     o[b,h,:] = sum_s exp(m_s - m_g) o_s / l_g
+ * ("Flash decoding": Overview of the algorithm, combine equations, and its
+ * combine kernel -- one workgroup per (batch, head)).  Splits with
+ * m_s = -inf carry no keys and get weight 0.
+ *
+ *   o_part [B,H,n_splits,D], m_part, l_part [B,H,n_splits] float32 (as written
+ *   by attn_decode_split);  o [B,H,D] dtype, rounded to nearest-even.
+ *   Supported: D in {64, 128}; dtype F16, BF16, F32; n_splits >= 1.
+ */
+fa2_status attn_decode_combine(const float *o_part, const float *m_part, const float *l_part,
+                               void *o, int B, int H, int D, int n_splits,
+                               fa2_dtype dtype, void *stream);
+
+/*
+ * attn_decode_default_splits -- split count for attn_decode_split that fills
+ * the current device ("Flash decoding": many blocks each reading a chunk of
+ * the cache is what lets the read use the memory bandwidth).  Picks the
+ * count so that B*H*n_splits workgroups cover the device's compute units in
+ * whole waves of residency, with at least 256 keys per split.  Returns a value
+ * >= 1; if the device cannot be queried it assumes 256 compute units.
+ */
+int attn_decode_default_splits(int B, int H, int N, int D);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *fa2_status_string(fa2_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H */

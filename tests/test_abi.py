@@ -1,0 +1,112 @@
+"""The C ABI without a GPU: the library loads, exports exactly what
+include/fa2.h declares, and rejects bad arguments with a status code before
+anything is enqueued.  No compute call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_attention_fa2_amd import fa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa2.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa2.LIB_PATH),
+                                reason="libfa2.so not built (run __graft_entry__.build())")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+
+
+def test_exports_match_header():
+    declared = header_functions()
+    assert declared == set(fa2.EXPORTS)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", fa2.LIB_PATH], text=True)
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert declared <= exported, declared - exported
+    # nothing else of ours leaks out of the library
+    ours = {s for s in exported if "fa2" in s or s.startswith("attn")}
+    assert ours == declared
+
+
+def test_status_strings():
+    L = fa2.lib()
+    for code, text in fa2.STATUS.items():
+        assert L.fa2_status_string(code).decode() == text
+    assert L.fa2_status_string(99).decode() == "unknown status"
+
+
+def _fwd(q=1, k=1, v=1, o=1, lse=None, B=1, H=1, Nq=4, Nk=4, D=64, scale=0.125, causal=0,
+         dt=fa2.FA2_F16):
+    p = lambda x: None if x is None else ctypes.c_void_p(x * 4096)  # noqa: E731
+    return fa2.lib().attn_fwd(p(q), p(k), p(v), p(o), p(lse), B, H, Nq, Nk, D, scale, causal, dt,
+                              None)
+
+
+def test_fwd_error_paths():
+    assert _fwd(Nk=0) == 2
+    assert _fwd(B=-1) == 2
+    assert _fwd(D=0) == 2
+    assert _fwd(D=128) == 3
+    assert _fwd(D=32) == 3
+    assert _fwd(dt=7) == 3
+    assert _fwd(causal=1, Nq=4, Nk=8) == 3
+    assert _fwd(causal=2) == 3
+    assert _fwd(q=None) == 1
+    assert _fwd(v=None) == 1
+    L = fa2.lib()
+    mis = ctypes.c_void_p(4096 + 8)
+    ok = ctypes.c_void_p(4096)
+    assert L.attn_fwd(mis, ok, ok, ok, None, 1, 1, 4, 4, 64, 0.1, 0, 1, None) == 4
+    assert L.attn_fwd(ok, ok, ok, ok, ctypes.c_void_p(4098), 1, 1, 4, 4, 64, 0.1, 0, 1, None) == 4
+    # a slice of 2 GiB or more is refused up front
+    assert _fwd(Nk=1 << 24, D=64) == 3
+
+
+def test_fwd_empty_outputs_enqueue_nothing():
+    # zero rows: valid and a no-op, even with NULL pointers
+    assert fa2.lib().attn_fwd(None, None, None, None, None, 0, 1, 4, 4, 64, 0.1, 0, 1, None) == 0
+    assert fa2.lib().attn_fwd(None, None, None, None, None, 1, 1, 0, 4, 64, 0.1, 0, 1, None) == 0
+
+
+def test_decode_error_paths():
+    L = fa2.lib()
+    ok = ctypes.c_void_p(4096)
+    args = lambda **kw: dict(dict(B=1, H=1, N=64, D=128, ns=4, dt=1), **kw)  # noqa: E731
+
+    def split(q=ok, **kw):
+        a = args(**kw)
+        return L.attn_decode_split(q, ok, ok, ok, ok, ok, a["B"], a["H"], a["N"], a["D"], 0.1,
+                                   a["ns"], a["dt"], None)
+
+    assert split(N=0) == 2
+    assert split(ns=0) == 2
+    assert split(D=96) == 3
+    assert split(dt=5) == 3
+    assert split(q=None) == 1
+    assert split(q=ctypes.c_void_p(4100)) == 4
+    assert split(B=0) == 0
+    assert L.attn_decode_combine(ok, ok, ok, ok, 1, 1, 128, 0, 1, None) == 2
+    assert L.attn_decode_combine(ok, ok, ok, None, 1, 1, 128, 4, 1, None) == 1
+    assert L.attn_decode_combine(ok, ok, ok, ok, 1, 1, 80, 4, 1, None) == 3
+    assert L.attn_decode_combine(ok, ok, ok, ok, 0, 1, 128, 4, 1, None) == 0
+
+
+def test_default_splits_host_logic():
+    L = fa2.lib()
+    for B, H, N in ((8, 32, 32768), (1, 1, 100), (1, 1, 1 << 20), (64, 64, 4096)):
+        s = L.attn_decode_default_splits(B, H, N, 128)
+        assert 1 <= s <= max(1, (N + 255) // 256)
+    assert L.attn_decode_default_splits(0, 1, 10, 128) == 1
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa2, "_lib", None)
+    monkeypatch.setattr(fa2, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        fa2.lib()

@@ -1,0 +1,192 @@
+"""GPU parity of attn_fwd against the fp64 oracle, through the C ABI.
+
+Tolerances (max abs on O): 1e-4 for f32 I/O, 4e-3 for f16/bf16 I/O; LSE
+1e-4.  Inputs are the seeded N(0,1) workloads of workloads.py plus ragged and
+degenerate cases.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from exact_attention_fa2_amd import fa2, inputs, workloads
+from gpu_util import (LSE_TOL, TOL, assert_close, download_f64, edge_tol, seeded, torch_dtype,
+                      upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(q, k, v, dt, scale, causal, lse=True):
+    tq, tk, tv = upload(q, dt), upload(k, dt), upload(v, dt)
+    out = fa2.attn_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=lse)
+    import torch
+    torch.cuda.synchronize()
+    if lse:
+        return download_f64(out[0]), download_f64(out[1])
+    return download_f64(out), None
+
+
+def check_full(cfg, rows=None, edge=False):
+    """Compare with the oracle.  ``edge`` selects the bound for cases outside
+    the named workloads (see gpu_util.edge_tol); named workloads use the plain
+    bar."""
+    q, k, v = seeded(cfg.B, cfg.H, cfg.Nq, cfg.Nk, cfg.D, cfg.dtype, cfg.seed)
+    o, lse = run_fwd(q, k, v, cfg.dtype, cfg.scale, cfg.causal)
+    q64, k64, v64 = (inputs.to_f64(x, cfg.dtype) for x in (q, k, v))
+    if rows is None:
+        ro, rl = oracle.attn(q64, k64, v64, cfg.scale, cfg.causal)
+        tol = edge_tol(cfg.dtype, ro) if edge else TOL[cfg.dtype]
+        assert_close(cfg.name + " O", o, ro, tol)
+        assert_close(cfg.name + " LSE", lse, rl, LSE_TOL)
+    else:
+        ro, rl = oracle.attn_rows(q64, k64, v64, cfg.scale, cfg.causal, rows)
+        assert_close(cfg.name + " O (sampled rows)", o.reshape(-1, cfg.D)[rows], ro, TOL[cfg.dtype])
+        assert_close(cfg.name + " LSE (sampled rows)", lse.reshape(-1)[rows], rl, LSE_TOL)
+
+
+def test_tiny_f32():
+    check_full(workloads.TINY_F32)
+
+
+def test_headline_f32_4096():
+    check_full(workloads.HEADLINE_F32)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("n", [512, 1024])
+def test_multihead_full(n, dt):
+    check_full(workloads.multihead(n, dt))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_multihead_2048_sampled(dt):
+    cfg = workloads.multihead(2048, dt)
+    g = np.random.default_rng(1)
+    total = cfg.B * cfg.H * cfg.Nq
+    # every row of the first and last head plus 1024 random rows
+    rows = np.unique(np.concatenate([np.arange(cfg.Nq), np.arange(total - cfg.Nq, total),
+                                     g.choice(total, 1024, replace=False)]))
+    check_full(cfg, rows)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_causal_lse_f16(causal):
+    check_full(workloads.causal_lse(causal))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_causal_lse_shape_in_bf16(causal):
+    """The causal workload's shape in bf16 (not a named workload): early causal
+    rows average few keys, so |O| reaches ~3 and the bf16 format bound applies."""
+    c = workloads.causal_lse(causal)
+    cfg = workloads.Prefill(c.name + " bf16", c.B, c.H, c.Nq, c.Nk, c.D, "bf16", c.scale,
+                            c.causal, c.seed)
+    check_full(cfg, edge=True)
+
+
+RAGGED = [  # (B, H, Nq, Nk, causal)
+    (1, 1, 1, 1, False), (1, 1, 1, 1, True), (2, 3, 77, 131, False), (1, 2, 200, 200, True),
+    (3, 1, 129, 65, False), (1, 1, 17, 1000, False), (2, 2, 300, 300, True),
+    (1, 4, 129, 129, True), (1, 1, 64, 1, False),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_ragged_and_degenerate(shape, dt):
+    B, H, Nq, Nk, causal = shape
+    cfg = workloads.Prefill("ragged", B, H, Nq, Nk, 64, dt, 0.125, causal, 3)
+    check_full(cfg, edge=True)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_tile_grid_not_multiple_of_eight(dt):
+    # 3 heads x 3 query tiles: the XCD remap is skipped when the tile count is not a multiple of 8
+    cfg = workloads.Prefill("odd grid", 1, 3, 384, 256, 64, dt, 0.125, False, 4)
+    check_full(cfg, edge=True)
+    cfg = workloads.Prefill("odd grid causal", 1, 3, 384, 384, 64, dt, 0.125, True, 4)
+    check_full(cfg, edge=True)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_identity_values_rows_sum_to_one(dt):
+    """V = I with Nk = D = 64: O is the probability matrix; rows sum to 1."""
+    q, k, _ = seeded(1, 2, 100, 64, 64, dt, 7)
+    eye = np.broadcast_to(np.eye(64, dtype=np.float32), (1, 2, 64, 64)).copy()
+    v = inputs.f32_to_bf16_bits(eye) if dt == "bf16" else eye.astype(
+        inputs.storage_numpy_dtype(dt))
+    o, _ = run_fwd(q, k, v, dt, 0.3, False)
+    # P is rounded to the storage dtype before the PV product (relative 2^-11
+    # for f16, 2^-9 for bf16) and each output once more, so a row sum can
+    # drift by twice that relative step; f32 keeps full precision.
+    sums = o.sum(axis=-1)
+    bound = {"f32": 1e-5, "f16": 2e-3, "bf16": 8e-3}[dt]
+    assert np.max(np.abs(sums - 1.0)) <= bound, np.max(np.abs(sums - 1.0))
+    ro, _ = oracle.attn(inputs.to_f64(q, dt), inputs.to_f64(k, dt), inputs.to_f64(v, dt), 0.3)
+    assert_close("V=I " + dt, o, ro, edge_tol(dt, ro))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_keys_give_mean_of_values(dt, causal):
+    q, _, v = seeded(1, 1, 256, 256, 64, dt, 8)
+    k = np.zeros_like(q)
+    o, lse = run_fwd(q, k, v, dt, 0.125, causal)
+    v64 = inputs.to_f64(v, dt)[0, 0]
+    if causal:
+        want = np.cumsum(v64, axis=0) / np.arange(1, 257)[:, None]
+        want_lse = np.log(np.arange(1, 257))
+    else:
+        want = np.broadcast_to(v64.mean(axis=0), (256, 64))
+        want_lse = np.full(256, np.log(256))
+    assert_close("K=0 " + dt, o[0, 0], want, edge_tol(dt, want))
+    assert_close("K=0 LSE " + dt, lse[0, 0], want_lse, LSE_TOL)
+    if causal:  # row 0 sees key 0 alone: exactly V_0
+        assert np.array_equal(o[0, 0, 0], v64[0])
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_large_score_shift_is_safe(dt):
+    """Scores far past exp's f32 overflow (about 88) must not overflow: the
+    kernels subtract the running max.  K' = K + u shifts every score of row i
+    by the same scale*q_i.u, and GPU(K') is compared with oracle(K')."""
+    q, k, v = seeded(1, 2, 130, 190, 64, dt, 9)
+    k64 = inputs.to_f64(k, dt)
+    k64[..., :4] += 64.0
+    k32 = k64.astype(np.float32)
+    k2 = inputs.f32_to_bf16_bits(k32) if dt == "bf16" else k32.astype(inputs.storage_numpy_dtype(dt))
+    o, lse = run_fwd(q, k2, v, dt, 0.5, False)
+    ro, rl = oracle.attn(inputs.to_f64(q, dt), inputs.to_f64(k2, dt), inputs.to_f64(v, dt), 0.5)
+    assert np.max(np.abs(rl)) > 100
+    assert np.all(np.isfinite(o))
+    # Each score is now a float32 sum whose terms reach ~100, so it carries an
+    # absolute rounding error of a few ulp(128) = 1.5e-5; the softmax weights
+    # inherit that as a relative error, which can exceed the 1e-4 f32 bar on
+    # O.  Half-precision inputs keep their own (looser) bar.
+    tol = 5e-4 if dt == "f32" else edge_tol(dt, ro)
+    assert_close("shift O " + dt, o, ro, tol)
+    assert_close("shift LSE " + dt, lse, rl, 1e-4 * max(1.0, float(np.max(np.abs(rl)))))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_deterministic(dt):
+    import torch
+    q, k, v = seeded(2, 4, 300, 300, 64, dt, 10)
+    tq, tk, tv = upload(q, dt), upload(k, dt), upload(v, dt)
+    a = fa2.attn_fwd(tq, tk, tv, scale=0.125, causal=True, return_lse=True)
+    b = fa2.attn_fwd(tq, tk, tv, scale=0.125, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_lse_optional_and_stream_order():
+    import torch
+    q, k, v = seeded(1, 2, 256, 256, 64, "f16", 11)
+    tq, tk, tv = upload(q, "f16"), upload(k, "f16"), upload(v, "f16")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o1 = fa2.attn_fwd(tq, tk, tv, scale=0.125)
+    s.synchronize()
+    o2, _ = fa2.attn_fwd(tq, tk, tv, scale=0.125, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert o1.dtype == torch_dtype("f16")
