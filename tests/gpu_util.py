@@ -52,16 +52,19 @@ def bf16_half_ulp(x):
     return 2.0 ** (np.floor(np.log2(a)) - 8)
 
 
-def edge_tol(dt, ref):
+def edge_tol(dt, ref, got=None):
     """Bound for cases outside the named N(0,1) workloads.
 
     f32 and f16 keep the plain bar.  A bf16 output cannot be closer to an
     exact value than half a bf16 spacing, which is 3.9e-3 on [1,2) and 7.8e-3
     on [2,4) -- at or above the 4e-3 bar -- so for bf16 the bar is 4e-3 of
-    arithmetic error on top of that unavoidable rounding of the result."""
+    arithmetic error on top of that unavoidable rounding of the result.  The
+    spacing is taken at the larger of |ref| and |got|, since a result that
+    rounds across a power of two takes the spacing of the upper binade."""
     if dt != "bf16":
         return TOL[dt]
-    return TOL[dt] + bf16_half_ulp(ref)
+    mag = np.abs(ref) if got is None else np.maximum(np.abs(ref), np.abs(got))
+    return TOL[dt] + bf16_half_ulp(mag)
 
 
 def seeded(B, H, Nq, Nk, D, dt, seed):
