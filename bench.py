@@ -54,6 +54,33 @@ def cpu_baseline(cfg):
             "sample": "%s, all %d rows, fp64, %.2f s wall" % (cfg.name, cfg.B * cfg.H * cfg.Nq, dt)}
 
 
+def measured_traffic():
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (profiles/traffic.json, written from a profile of this bench), each scaled
+    by the counter's reading for a plain device copy of known size.  None when
+    absent or when it was taken on a different version of a kernel."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    out = {}
+    for name, rec in data.get("kernels", {}).items():
+        if rec.get("source_sha") == kernel_source_sha(rec.get("source", "")):
+            out[name] = rec.get("bytes_per_launch")
+    return out
+
+
+def kernel_source_sha(rel):
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()[:16]
+    except OSError:
+        return None
+
+
 def upload(a, dt):
     import numpy as np
     import torch
@@ -103,11 +130,25 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--decode-dtype", default="f16", choices=["f16", "bf16"])
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (to scale the FETCH_SIZE "
+                         "and WRITE_SIZE counters of a profile) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the path has no multi-GPU form "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        import torch
+        torch.cuda.set_device(0)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "calls": 5}))
+        return
 
     from exact_attention_fa2_amd import fa2, workloads
     pre = workloads.HEADLINE_F32
@@ -126,6 +167,8 @@ def main():
 
     pq, pk, pv = prefill_inputs(pre)
     po = torch.empty_like(pq)
+    need = fa2.workspace_size(pre.B, pre.H, pre.Nq, pre.Nk, pre.D, pre.causal, fa2.FA2_F32)
+    pws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     log("decode inputs: generating %s" % dec.name)
     dq, dk, dv = decode_inputs(dec)
     ns = fa2.default_splits(dec.B, dec.H, dec.N, dec.D)
@@ -135,7 +178,7 @@ def main():
     do = torch.empty((dec.B, dec.H, dec.D), dtype=dq.dtype, device="cuda")
 
     def prefill():
-        fa2.attn_fwd(pq, pk, pv, scale=pre.scale, out=po)
+        fa2.attn_fwd(pq, pk, pv, scale=pre.scale, out=po, workspace=pws)
 
     def split():
         fa2.attn_decode_split(dq, dk, dv, dec.scale, ns, op, mp, lp)
@@ -197,6 +240,7 @@ def main():
                                                                      100 * tf / PEAK_F16))
             del q, k, v, o, lse
 
+    traffic = measured_traffic()
     line = {
         "metric": "attention fwd TFLOP/s (N=4096,D=64) + decode KV GB/s; % of roofline",
         "value": round(tflops, 3),
@@ -219,14 +263,15 @@ def main():
                        "n_splits": ns},
         },
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_F32,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_F32, 4), "traffic": None,
-                     "kernel": "fwd_f32_d64", "us": round(pre_ms * 1e3, 3)},
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_F32, 4),
+                     "traffic": traffic.get("fwd_f32"), "kernel": "fwd_f32_d64",
+                     "us": round(pre_ms * 1e3, 3)},
         "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "us": round(dec_ms * 1e3, 2),
                    "split_us": round(split_ms * 1e3, 2), "combine_us": round(comb_ms * 1e3, 2),
                    "bytes": dec.kv_bytes},
         "roofline_decode": {"bound": "hbm", "achieved": round(split_gbs, 1), "peak": PEAK_HBM,
                             "unit": "GB/s", "frac": round(split_gbs / PEAK_HBM, 4),
-                            "traffic": None, "kernel": "decode_split",
+                            "traffic": traffic.get("decode_split"), "kernel": "decode_split",
                             "us": round(split_ms * 1e3, 2)},
         "extra": extra,
         "cpu_baseline": base,

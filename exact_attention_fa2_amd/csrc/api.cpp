@@ -45,9 +45,11 @@ bool valid_dtype(int dt) { return dt == FA2_F32 || dt == FA2_F16 || dt == FA2_BF
 
 }  // namespace
 
-FA2_API fa2_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
-                            int B, int H, int Nq, int Nk, int D, float scale, int causal,
-                            fa2_dtype dtype, void *stream) {
+namespace {
+
+fa2_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                    int Nq, int Nk, int D, float scale, int causal, fa2_dtype dtype,
+                    void *workspace, size_t workspace_bytes, void *stream) {
     if (B < 0 || H < 0 || Nq < 0 || Nk < 1 || D < 1) return FA2_ERR_SHAPE;
     if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
     if (causal != 0 && causal != 1) return FA2_ERR_UNSUPPORTED;
@@ -56,7 +58,7 @@ FA2_API fa2_status attn_fwd(const void *q, const void *k, const void *v, void *o
     if ((long long)B * H * Nq == 0) return FA2_OK;  // nothing to compute
     if (!q || !k || !v || !o) return FA2_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-        (lse && ((uintptr_t)lse & 3u)))
+        (lse && ((uintptr_t)lse & 3u)) || (workspace && !aligned16(workspace)))
         return FA2_ERR_ALIGN;
     const long long es = esize(dtype);
     if ((long long)Nk * D * es > kMaxSliceBytes || (long long)Nq * D * es > kMaxSliceBytes)
@@ -64,10 +66,36 @@ FA2_API fa2_status attn_fwd(const void *q, const void *k, const void *v, void *o
     if ((long long)B * H > 65535) return FA2_ERR_UNSUPPORTED;
     const DeviceInfo *dev = current_device();
     if (!dev) return FA2_ERR_DEVICE;
-    fa2::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, scale, causal, dev->num_cus};
+    fa2::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, scale, causal, dev->num_cus,
+                   workspace, workspace ? workspace_bytes : 0};
     hipStream_t st = (hipStream_t)stream;
     if (dtype == FA2_F32) return fa2::launch_fwd_f32_d64(a, st);
     return fa2::launch_fwd_mfma_d64(a, dtype, st);
+}
+
+}  // namespace
+
+FA2_API fa2_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                            fa2_dtype dtype, void *stream) {
+    return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, nullptr, 0, stream);
+}
+
+FA2_API fa2_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+                               int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                               fa2_dtype dtype, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, workspace,
+                    workspace_bytes, stream);
+}
+
+FA2_API size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int causal,
+                                       fa2_dtype dtype) {
+    (void)causal;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D != 64 || dtype != FA2_F32) return 0;
+    int cus = 256;
+    if (const DeviceInfo *dev = current_device()) cus = dev->num_cus;
+    return fa2::f32_workspace_bytes(B, H, Nq, Nk, cus);
 }
 
 FA2_API fa2_status attn_decode_split(const void *q, const void *k, const void *v,

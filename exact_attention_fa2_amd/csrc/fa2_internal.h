@@ -23,9 +23,12 @@ struct FwdArgs {
     float scale;
     int causal;
     int num_cus;
+    void *ws;         // optional device workspace (may be null)
+    size_t ws_bytes;  // its size
 };
 
 fa2_status launch_fwd_f32_d64(const FwdArgs &a, hipStream_t st);
+size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int num_cus);
 fa2_status launch_fwd_mfma_d64(const FwdArgs &a, fa2_dtype dt, hipStream_t st);
 
 struct DecodeArgs {
@@ -37,6 +40,11 @@ struct DecodeArgs {
 };
 
 fa2_status launch_decode_split(const DecodeArgs &a, fa2_dtype dt, hipStream_t st);
+// Merge per-row partials [rows][n_splits][D] (natural-log m) into o [rows][D]
+// of dtype dt and, if lse is not null, lse [rows].
+fa2_status launch_combine_rows(const float *o_part, const float *m_part, const float *l_part,
+                               void *o, float *lse, size_t rows, int D, int n_splits, fa2_dtype dt,
+                               hipStream_t st);
 fa2_status launch_decode_combine(const float *o_part, const float *m_part, const float *l_part,
                                  void *o, int B, int H, int D, int n_splits, fa2_dtype dt,
                                  hipStream_t st);

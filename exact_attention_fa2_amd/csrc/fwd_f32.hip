@@ -5,25 +5,29 @@
 // Method ("Flash attention, f32": sections One block of queries per CTA, The
 // loop over keys, Online softmax, After the loop; "Flash Attention"
 // (aarnphm.xyz): Deriving the online softmax, tile form).  A workgroup owns 16
-// query rows.  Its 8 waves each walk a contiguous slice of the keys, 16 keys a
+// query rows.  Its 16 waves each walk a contiguous slice of the keys, 16 keys a
 // step, carrying the running max m, the running denominator l and the
 // unnormalised output O, rescaled by exp(m_old - m_new) whenever the max grows.
-// At the end the 8 partial states are merged with the (m, l) monoid of "Flash
+// At the end the 16 partial states are merged with the (m, l) monoid of "Flash
 // Attention" (section Deriving the online softmax) through LDS, then O/l and
 // LSE = m + ln l are written.
 //
 // Why split the keys across waves: one head of 4096 rows gives only 256 tiles
-// of 16 rows, one per compute unit; splitting each tile's keys 8 ways puts two
-// waves on every SIMD.  The pages' FlashAttention-2 prefers splitting queries
-// across warps ("Flash Attention", section FlashAttention 2); this kernel keeps
-// that across workgroups and splits keys only inside one.
+// of 16 rows, one per compute unit; splitting each tile's keys 16 ways puts
+// four waves on every SIMD, enough to keep the matrix cores fed while other
+// waves wait for their K/V loads.  The pages' FlashAttention-2 prefers
+// splitting queries across warps ("Flash Attention", section FlashAttention 2);
+// this kernel keeps that across workgroups and splits keys only inside one.
 //
 // Lane layout (lane = 16*g + c):
-//   S^T = K Q^T per 16-key step: lane holds scores of query c for keys 4g..4g+3.
+//   S^T = K Q^T per 16-key step: lane holds scores of query c for keys 4g..4g+3;
+//   MFMA i pairs K and Q at d = 16*(i/4) + 4g + i%4 in lane group g.
 //   O^T = V^T P^T: lane holds O[query c][16g .. 16g+15] (the MFMA's n index is
 //   permuted so that each lane's V operand is one 16-byte row segment).
 // The contraction index of both products is only a pairing of operand slots,
 // so A and B just have to agree on it.
+#include <algorithm>
+
 #include "fa2_device.h"
 #include "fa2_internal.h"
 
@@ -33,19 +37,19 @@ namespace {
 
 constexpr int kD = 64;
 constexpr int kQT = 16;     // query rows per workgroup
-constexpr int kWaves = 8;   // waves per workgroup, each on its own key slice
+constexpr int kWaves = 16;  // waves per workgroup (4 per SIMD), each on its own key slice
 constexpr int kStep = 16;   // keys per step
 
 struct KVRegs {
-    f32x4 k[4];   // K[key k0 + c][16g .. 16g+15]
-    f32x4 v[4];   // V[key k0 + 4g + t][4c .. 4c+3], t = 0..3
+    f32x4 k[4];   // k[j] = K[key k0 + c][16j + 4g .. 16j + 4g + 3]
+    f32x4 v[4];   // v[t] = V[key k0 + 4g + t][4c .. 4c+3], t = 0..3
 };
 
 __device__ __forceinline__ void load_kv(KVRegs &r, __amdgpu_buffer_rsrc_t rk,
                                         __amdgpu_buffer_rsrc_t rv, int k0, int g, int c) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        r.k[j] = __builtin_bit_cast(f32x4, load16(rk, (uint32_t)(((k0 + c) * kD + 16 * g + 4 * j) * 4)));
+        r.k[j] = __builtin_bit_cast(f32x4, load16(rk, (uint32_t)(((k0 + c) * kD + 16 * j + 4 * g) * 4)));
 #pragma unroll
     for (int t = 0; t < 4; ++t)
         r.v[t] = __builtin_bit_cast(f32x4, load16(rv, (uint32_t)(((k0 + 4 * g + t) * kD + 4 * c) * 4)));
@@ -60,7 +64,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
     __shared__ float s_l[kWaves][kQT];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave index as a wave-uniform value, so the key loop below is scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c = lane & 15;
     const int q0 = blockIdx.x * kQT;
     const int bh = blockIdx.y;
@@ -72,11 +77,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
     const auto rk = make_rsrc(Kh, (uint32_t)Nk * kD * 4);
     const auto rv = make_rsrc(Vh, (uint32_t)Nk * kD * 4);
 
-    // Q^T operand of S^T = K Q^T: slot i of lane (g,c) is Q[q0 + c][16g + i].
+    // Q^T operand of S^T = K Q^T: slot i of lane (g,c) is Q[q0 + c][d(g,i)]
+    // with d(g,i) = 16*(i/4) + 4g + i%4 -- any pairing of the contraction index
+    // works, and this one lets the four lanes of a key row read 64 contiguous
+    // bytes of K per load instruction.
     float qv[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        f32x4 t = __builtin_bit_cast(f32x4, load16(rq, (uint32_t)(((q0 + c) * kD + 16 * g + 4 * j) * 4)));
+        f32x4 t = __builtin_bit_cast(f32x4, load16(rq, (uint32_t)(((q0 + c) * kD + 16 * j + 4 * g) * 4)));
         qv[4 * j + 0] = t[0];
         qv[4 * j + 1] = t[1];
         qv[4 * j + 2] = t[2];
@@ -95,24 +103,38 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    KVRegs cur, nxt;
-    if (st0 < st1) load_kv(cur, rk, rv, st0 * kStep, g, c);
-    for (int st = st0; st < st1; ++st) {
+    // One 16-key step on the registers in `cur`; the next step's K/V are
+    // loaded into `nxt` first so the loads overlap this step's work.  The load
+    // is issued on every step, also the last (it then reads past this wave's
+    // keys, harmlessly: in-slice data or zeros from the buffer descriptor), so
+    // the compiler's count of loads in flight is the same on every path and its
+    // wait for `cur` never also waits for `nxt`.
+    auto step = [&](int st, const KVRegs &cur, KVRegs &nxt) {
         const int k0 = st * kStep;
-        if (st + 1 < st1) load_kv(nxt, rk, rv, k0 + kStep, g, c);
+        load_kv(nxt, rk, rv, k0 + kStep, g, c);
+        // keep the loads here: without this the scheduler sinks them next to
+        // their use in the following step, which serialises load and compute
+        __builtin_amdgcn_sched_barrier(0);
 
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+        // two independent accumulation chains, summed at the end
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, sacc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+        for (int i = 0; i < 16; i += 2) {
             sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.k[i >> 2][i & 3], qv[i], sacc, 0, 0, 0);
+            sacc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.k[i >> 2][(i & 3) + 1], qv[i + 1], sacc2,
+                                                        0, 0, 0);
+        }
+        sacc += sacc2;
 
-        // sacc[r] = S[query q0 + c][key k0 + 4g + r]
+        // sacc[r] = S[query q0 + c][key k0 + 4g + r]; a step past this wave's
+        // slice is masked entirely and leaves the state unchanged
         float s[4];
         float mx = -INFINITY;
+        const bool in_slice = st < st1;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int key = k0 + 4 * g + r;
-            bool live = key < Nk;
+            bool live = in_slice && key < Nk;
             if (CAUSAL) live = live && key <= q0 + c;
             s[r] = live ? sacc[r] * scale_log2 : -INFINITY;
             mx = fmaxf(mx, s[r]);
@@ -139,7 +161,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
             for (int j = 0; j < 4; ++j)
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.v[t][j], p[t], acc[j], 0, 0, 0);
         m = m_new;
-        if (st + 1 < st1) cur = nxt;
+    };
+
+    // Steps run in pairs, unconditionally, so each step's prefetch has a
+    // use on every path and the compiler keeps it where it is issued.
+    KVRegs ra, rb;
+    load_kv(ra, rk, rv, st0 * kStep, g, c);
+    for (int st = st0; st < st1; st += 2) {
+        step(st, ra, rb);
+        step(st + 1, rb, ra);
     }
 
     // acc[j][r] = O[q0 + c][16g + 4r + j]; the lane's l covers keys 4g..4g+3 of each step.
@@ -155,41 +185,325 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
             f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
     __syncthreads();
 
-    // Merge the 8 wave states of each row: 512 threads, 2 output columns each.
-    const int row = threadIdx.x >> 5;
-    const int d = (threadIdx.x & 31) * 2;
+    // Merge the 16 wave states of each row: one output element per thread.
+    const int row = threadIdx.x >> 6;
+    const int d = threadIdx.x & 63;
     float mg = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mg = fmaxf(mg, s_m[w][row]);
-    float lg = 0.f, o0 = 0.f, o1 = 0.f;
+    float lg = 0.f, o0 = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
         const float mw = s_m[w][row];
         const float wt = mw == -INFINITY ? 0.f : exp2f_fast(mw - mg);
         lg += wt * s_l[w][row];
         o0 += wt * s_o[w][row][d];
-        o1 += wt * s_o[w][row][d + 1];
     }
     const int qrow = q0 + row;
     if (qrow < Nq) {
-        const float inv = 1.f / lg;
-        float *orow = O + ((size_t)bh * Nq + qrow) * kD;
-        orow[d] = o0 * inv;
-        orow[d + 1] = o1 * inv;
+        O[((size_t)bh * Nq + qrow) * kD + d] = o0 / lg;
         if (LSE && d == 0) LSE[(size_t)bh * Nq + qrow] = (mg + log2f_fast(lg)) * kLn2;
     }
 }
 
+// ---------------------------------------------------------------------------
+// Shared-K/V variant with an optional split of the keys across workgroups.
+//
+// A workgroup owns 64 query rows (4 tiles of 16) and one chunk of the keys.
+// Its 16 waves are 4 query tiles x 4 key sub-slices; each K/V block of a
+// sub-slice is moved into LDS once (DMA) and read by the 4 waves of the 4
+// query tiles, so every byte fetched from L2 feeds 64 rows instead of 16.
+// When the keys are split into C chunks ("Flash decoding": split the keys,
+// keep unnormalised partials, merge with the (m, l) monoid), each workgroup
+// writes (O_s, m_s, l_s) for its rows and chunk and the decode combine kernel
+// merges them; with C = 1 it writes O and LSE itself.
+namespace shared {
+
+constexpr int kTiles = 4;                   // query tiles of 16 rows per workgroup
+constexpr int kSub = kWaves / kTiles;       // key sub-slices per workgroup
+constexpr int kRows = kTiles * kQT;         // 64 query rows per workgroup
+constexpr int kBlkBytes = kStep * kD * 4;   // 4 KB: one 16-key block of K (or V)
+constexpr int kBufBytes = kSub * 2 * kBlkBytes;  // K and V blocks of all sub-slices
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(kWaves * 64, 1) void kernel(
+    const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
+    float *__restrict__ O, float *__restrict__ LSE, float *__restrict__ o_part,
+    float *__restrict__ m_part, float *__restrict__ l_part, int Nq, int Nk, float scale_log2) {
+    // Two K/V buffers (separate arrays, so DMA into one is seen not to alias
+    // reads of the other); after the loop the same 64 KB hold the merge.
+    __shared__ __attribute__((aligned(16))) char buf0[kBufBytes];
+    __shared__ __attribute__((aligned(16))) char buf1[kBufBytes];
+    __shared__ float s_m[kWaves][kQT];
+    __shared__ float s_l[kWaves][kQT];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int qa = wave & (kTiles - 1);  // query tile of this wave
+    const int ss = wave / kTiles;        // key sub-slice of this wave
+    const int g = lane >> 4, c = lane & 15;
+    const int q0 = blockIdx.x * kRows;
+    const int bh = blockIdx.y;
+    const int chunk = blockIdx.z, nchunks = gridDim.z;
+    const int qt0 = q0 + qa * kQT;  // first row of this wave's tile
+
+    const float *Qh = Q + (size_t)bh * Nq * kD;
+    const float *Kh = K + (size_t)bh * Nk * kD;
+    const float *Vh = V + (size_t)bh * Nk * kD;
+    const auto rq = make_rsrc(Qh, (uint32_t)Nq * kD * 4);
+    const auto rk = make_rsrc(Kh, (uint32_t)Nk * kD * 4);
+    const auto rv = make_rsrc(Vh, (uint32_t)Nk * kD * 4);
+
+    // Q^T operand, pairing d = 16*(i/4) + 4g + i%4 as in the kernel above.
+    float qv[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f32x4 t = __builtin_bit_cast(f32x4, load16(rq, (uint32_t)(((qt0 + c) * kD + 16 * j + 4 * g) * 4)));
+        qv[4 * j + 0] = t[0];
+        qv[4 * j + 1] = t[1];
+        qv[4 * j + 2] = t[2];
+        qv[4 * j + 3] = t[3];
+    }
+
+    // Steps of 16 keys: the chunk's steps, then this sub-slice's share.
+    const int kend = CAUSAL ? min(Nk, q0 + kRows) : Nk;
+    const int nsteps = (kend + kStep - 1) / kStep;
+    const int per_chunk = (nsteps + nchunks - 1) / nchunks;
+    const int c0 = chunk * per_chunk;
+    const int c1 = min(nsteps, c0 + per_chunk);
+    const int per_sub = max(0, (c1 - c0 + kSub - 1) / kSub);
+    auto sub_first = [&](int sub) { return c0 + sub * per_sub; };
+    const int st0 = sub_first(ss);
+    const int st1 = min(c1, st0 + per_sub);
+
+    // DMA of iteration `it` into a buffer: instruction I = 2*wave + i covers
+    // 1 KB; sub-slice I/8, part I%8 (0-3: K rows 4p..4p+3, 4-7: V rows).  K
+    // rows keep their 16-byte chunks XOR-swizzled by row, V rows are linear.
+    auto dma = [&](char *dst, int it) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int I = 2 * wave + i;
+            const int sub = I >> 3, part = I & 7;
+            const bool is_k = part < 4;
+            const int unit = (part & 3) * 64 + lane;  // 16-byte unit in the 4 KB block
+            const int row = unit >> 4, phys = unit & 15;
+            const int logical = is_k ? (phys ^ row) : phys;
+            const int key = (sub_first(sub) + it) * kStep + row;
+            // keys past the slice get an offset past the descriptor's range
+            // (zeros; never used): computed so that nothing can overflow
+            const uint32_t off =
+                key < Nk ? (uint32_t)key * (kD * 4) + (uint32_t)logical * 16 : 0xFFFFFFF0u;
+            char *blk = dst + (sub * 2 + (is_k ? 0 : 1)) * kBlkBytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_k ? rk : rv, (lds_void *)(blk + (part & 3) * 1024),
+                                                     16, off, 0, 0, 0);
+        }
+    };
+
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // This step's K and V operands, read from LDS into registers.
+    auto fetch = [&](const char *bufc, f32x4 *kr, f32x4 *vr) {
+        const char *kb = bufc + (ss * 2) * kBlkBytes;
+        const char *vb = kb + kBlkBytes;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            kr[j] = *reinterpret_cast<const f32x4 *>(kb + c * 256 + (((4 * j + g) ^ c) << 4));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            vr[t] = *reinterpret_cast<const f32x4 *>(vb + (4 * g + t) * 256 + (c << 4));
+    };
+
+    auto step = [&](const f32x4 *kr, const f32x4 *vr, int it) {
+        const int st = st0 + it;
+        const int k0 = st * kStep;
+
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, sacc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[i >> 2][i & 3], qv[i], sacc, 0, 0, 0);
+            sacc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[i >> 2][(i & 3) + 1], qv[i + 1], sacc2,
+                                                        0, 0, 0);
+        }
+        sacc += sacc2;
+        const bool in_slice = st < st1;
+        float sv[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key = k0 + 4 * g + r;
+            bool live = in_slice && key < Nk;
+            if (CAUSAL) live = live && key <= qt0 + c;
+            sv[r] = live ? sacc[r] * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sv[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float corr = exp2f_fast(m - m_use);
+        float p[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            p[r] = exp2f_fast(sv[r] - m_use);
+            psum += p[r];
+        }
+        l = l * corr + psum;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] *= corr;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[t][j], p[t], acc[j], 0, 0, 0);
+        m = m_new;
+    };
+
+    // Iterations: every sub-slice advances one step per iteration.  On entry
+    // to iteration it the buffer for it is in LDS; the DMA for it+1 goes to
+    // the other buffer, last read in iteration it-1.
+    // The operands are read before the next DMA is issued: a read that comes
+    // after an LDS DMA in program order would make the compiler wait for that
+    // DMA, which it cannot tell writes the other buffer.
+    dma(buf0, 0);
+    f32x4 kr[4], vr[4];
+    for (int it = 0; it < per_sub; it += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        fetch(buf0, kr, vr);
+        if (it + 1 < per_sub) dma(buf1, it + 1);
+        step(kr, vr, it);
+        if (it + 1 < per_sub) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_barrier();
+            fetch(buf1, kr, vr);
+            if (it + 2 < per_sub) dma(buf0, it + 2);
+            step(kr, vr, it + 1);
+        }
+    }
+
+    // Merge the 4 sub-slice states of each row through LDS.
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // every wave is done with the K/V buffers
+    // [16 rows][64] floats per wave: waves 0-7 in buf0, 8-15 in buf1
+    static_assert(sizeof(buf0) >= (kWaves / 2) * kQT * kD * 4, "merge space");
+    auto wave_o = [&](int w) {
+        return reinterpret_cast<float *>(w < kWaves / 2 ? buf0 : buf1) + (w % (kWaves / 2)) * kQT * kD;
+    };
+    if (g == 0) {
+        s_m[wave][c] = m;
+        s_l[wave][c] = l;
+    }
+    {
+        float *mine = wave_o(wave);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<f32x4 *>(&mine[c * kD + 16 * g + 4 * r]) =
+                f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+    }
+    __syncthreads();
+
+    // 1024 threads, 64 rows x 64 columns: 4 consecutive columns per thread.
+    const int row = threadIdx.x >> 4;         // 0..63
+    const int d = (threadIdx.x & 15) * 4;
+    const int tile = row / kQT, rr = row % kQT;
+    float mg = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub) mg = fmaxf(mg, s_m[sub * kTiles + tile][rr]);
+    float lg = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub) {
+        const int w = sub * kTiles + tile;
+        const float mw = s_m[w][rr];
+        const float wt = mw == -INFINITY ? 0.f : exp2f_fast(mw - mg);
+        lg += wt * s_l[w][rr];
+        o += wt * *reinterpret_cast<const f32x4 *>(&wave_o(w)[rr * kD + d]);
+    }
+    const int qrow = q0 + row;
+    if (qrow >= Nq) return;
+    const size_t rowid = (size_t)bh * Nq + qrow;
+    if (!SPLIT) {
+        *reinterpret_cast<f32x4 *>(O + rowid * kD + d) = o / lg;
+        if (LSE && d == 0) LSE[rowid] = (mg + log2f_fast(lg)) * kLn2;
+    } else {
+        const size_t pidx = rowid * nchunks + chunk;
+        *reinterpret_cast<f32x4 *>(o_part + pidx * kD + d) = o;
+        if (d == 0) {
+            m_part[pidx] = mg == -INFINITY ? -INFINITY : mg * kLn2;  // natural-log units
+            l_part[pidx] = lg;
+        }
+    }
+}
+
+}  // namespace shared
+
 }  // namespace
 
+// Split plan for the shared kernel: number of key chunks (1 = no split).
+// Split only when even 16-row workgroups cannot cover the device: with one
+// 16-row workgroup per compute unit or more, the unsplit kernels measured
+// faster than split + combine.
+int f32_chunks(int B, int H, int Nq, int Nk, int num_cus) {
+    const long long groups = (long long)B * H * ((Nq + shared::kRows - 1) / shared::kRows);
+    const long long tiles16 = (long long)B * H * ((Nq + kQT - 1) / kQT);
+    if (groups >= num_cus || tiles16 >= num_cus) return 1;
+    const int nsteps = (Nk + kStep - 1) / kStep;
+    long long c = (num_cus + groups - 1) / groups;
+    c = std::min<long long>(c, std::max(1, nsteps / shared::kSub));  // >= one step per sub-slice
+    c = std::min<long long>(c, 64);
+    return (int)std::max<long long>(1, c);
+}
+
+size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int num_cus) {
+    const int c = f32_chunks(B, H, Nq, Nk, num_cus);
+    if (c <= 1) return 0;
+    return (size_t)B * H * Nq * c * (kD + 2) * sizeof(float);
+}
+
+#ifndef FA2_F32_SHARED
+#define FA2_F32_SHARED 1
+#endif
+
 fa2_status launch_fwd_f32_d64(const FwdArgs &a, hipStream_t st) {
-    const dim3 grid((a.Nq + kQT - 1) / kQT, a.B * a.H);
-    const dim3 block(kWaves * 64);
     const float sl2 = a.scale * kLog2e;
+    const long long groups = (long long)a.B * a.H * ((a.Nq + shared::kRows - 1) / shared::kRows);
+    const dim3 block(kWaves * 64);
+    if (FA2_F32_SHARED && groups >= a.num_cus) {
+        // enough 64-row groups to fill the device: share K/V, no split
+        const dim3 grid((a.Nq + shared::kRows - 1) / shared::kRows, a.B * a.H, 1);
+        auto k = a.causal ? shared::kernel<true, false> : shared::kernel<false, false>;
+        return launch(k, grid, block, st, (const float *)a.q, (const float *)a.k, (const float *)a.v,
+                      (float *)a.o, a.lse, (float *)nullptr, (float *)nullptr, (float *)nullptr,
+                      a.Nq, a.Nk, sl2);
+    }
+    const int c = f32_chunks(a.B, a.H, a.Nq, a.Nk, a.num_cus);
+    if (c > 1 && a.ws && a.ws_bytes >= f32_workspace_bytes(a.B, a.H, a.Nq, a.Nk, a.num_cus)) {
+        // few rows: split the keys into c chunks, then merge the partials
+        const size_t rows = (size_t)a.B * a.H * a.Nq;
+        float *o_part = (float *)a.ws;
+        float *m_part = o_part + rows * c * kD;
+        float *l_part = m_part + rows * c;
+        const dim3 grid((a.Nq + shared::kRows - 1) / shared::kRows, a.B * a.H, c);
+        auto k = a.causal ? shared::kernel<true, true> : shared::kernel<false, true>;
+        fa2_status s = launch(k, grid, block, st, (const float *)a.q, (const float *)a.k,
+                              (const float *)a.v, (float *)a.o, a.lse, o_part, m_part, l_part, a.Nq,
+                              a.Nk, sl2);
+        if (s != FA2_OK) return s;
+        return launch_combine_rows(o_part, m_part, l_part, a.o, a.lse, rows, kD, c, FA2_F32, st);
+    }
+    // few rows and no workspace: 16-row workgroups fill the device instead
+    const dim3 grid((a.Nq + kQT - 1) / kQT, a.B * a.H);
     if (a.causal)
         return launch(fwd_f32_d64_kernel<true>, grid, block, st, (const float *)a.q,
-                      (const float *)a.k, (const float *)a.v, (float *)a.o, a.lse, a.Nq, a.Nk,
-                      sl2);
+                      (const float *)a.k, (const float *)a.v, (float *)a.o, a.lse, a.Nq, a.Nk, sl2);
     return launch(fwd_f32_d64_kernel<false>, grid, block, st, (const float *)a.q,
                   (const float *)a.k, (const float *)a.v, (float *)a.o, a.lse, a.Nq, a.Nk, sl2);
 }

@@ -18,8 +18,8 @@ STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "unsupported config
           4: "pointer not 16-byte aligned", 5: "kernel launch failed",
           6: "no usable gfx950 device"}
 
-EXPORTS = ("attn_fwd", "attn_decode_split", "attn_decode_combine",
-           "attn_decode_default_splits", "fa2_status_string")
+EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "attn_decode_split",
+           "attn_decode_combine", "attn_decode_default_splits", "fa2_status_string")
 
 _lib = None
 
@@ -41,6 +41,10 @@ def lib():
         vp, fp, i, f = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         L.attn_fwd.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp]
         L.attn_fwd.restype = i
+        L.attn_fwd_ws.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
+        L.attn_fwd_ws.restype = i
+        L.attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
+        L.attn_fwd_workspace_size.restype = ctypes.c_size_t
         L.attn_decode_split.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, f, i, i, vp]
         L.attn_decode_split.restype = i
         L.attn_decode_combine.argtypes = [fp, fp, fp, vp, i, i, i, i, i, vp]
@@ -86,10 +90,18 @@ def _contig(t, name):
         raise ValueError("%s must be contiguous" % name)
 
 
+def workspace_size(B, H, Nq, Nk, D, causal, dtype_code_) -> int:
+    return int(lib().attn_fwd_workspace_size(B, H, Nq, Nk, D, int(bool(causal)), dtype_code_))
+
+
 def attn_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=None,
-             stream=None):
+             stream=None, workspace=None, use_workspace=True):
     """Exact attention forward.  q [B,H,Nq,D], k/v [B,H,Nk,D] (same dtype).
 
+    When the library asks for a workspace for this shape (few rows: it then
+    splits the keys across workgroups), one is taken from ``workspace`` if
+    given and large enough, else allocated with torch for this call.
+    ``use_workspace=False`` calls the plain attn_fwd entry point instead.
     Returns o (and lse [B,H,Nq] float32 when ``return_lse``)."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -106,9 +118,21 @@ def attn_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse if return_lse else None),
-                        B, H, Nq, Nk, D, float(scale), int(bool(causal)), dtype_code(q),
-                        _stream(stream))
+    dc = dtype_code(q)
+    if not use_workspace:
+        st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                            _ptr(lse if return_lse else None), B, H, Nq, Nk, D, float(scale),
+                            int(bool(causal)), dc, _stream(stream))
+        _check("attn_fwd", st)
+        return (out, lse) if return_lse else out
+    need = workspace_size(B, H, Nq, Nk, D, causal, dc)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if need else 0
+    st = lib().attn_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse if return_lse else None),
+                           B, H, Nq, Nk, D, float(scale), int(bool(causal)), dc, ws_ptr, ws_bytes,
+                           _stream(stream))
     _check("attn_fwd", st)
     return (out, lse) if return_lse else out
 

@@ -43,7 +43,11 @@ def assert_close(name, got, want, tol):
     the outputs)."""
     e, msg = report(name, got, want)
     over = np.abs(got - want) - tol
-    assert np.all(over <= 0), msg + " > tol (worst excess %.3e)" % float(np.max(over))
+    if not np.all(over <= 0):
+        j = np.unravel_index(int(np.argmax(over)), over.shape)
+        tj = float(np.broadcast_to(tol, over.shape)[j])
+        raise AssertionError(msg + " > tol: worst excess %.3e at %s (got %.6g want %.6g tol %.3e)"
+                             % (float(over[j]), j, got[j], want[j], tj))
 
 
 def bf16_half_ulp(x):
@@ -52,19 +56,28 @@ def bf16_half_ulp(x):
     return 2.0 ** (np.floor(np.log2(a)) - 8)
 
 
-def edge_tol(dt, ref, got=None):
+def edge_tol(dt, ref, got=None, wabs=None):
     """Bound for cases outside the named N(0,1) workloads.
 
-    f32 and f16 keep the plain bar.  A bf16 output cannot be closer to an
-    exact value than half a bf16 spacing, which is 3.9e-3 on [1,2) and 7.8e-3
-    on [2,4) -- at or above the 4e-3 bar -- so for bf16 the bar is 4e-3 of
-    arithmetic error on top of that unavoidable rounding of the result.  The
-    spacing is taken at the larger of |ref| and |got|, since a result that
-    rounds across a power of two takes the spacing of the upper binade."""
+    f32 and f16 keep the plain bar.  bf16 carries two unavoidable roundings
+    that the named workloads (flat softmax, |O| < 1) never expose:
+      * the output itself: it cannot be closer to the exact value than half a
+        bf16 spacing, 3.9e-3 on [1,2) and 7.8e-3 on [2,4), taken at the larger
+        of |ref| and |got| (a result may round across a power of two);
+      * the weights: P is rounded to bf16 (relative 2^-9) before the P V
+        product, and normalising by the sum of the rounded weights moves each
+        normalised weight by at most about 2^-8 of itself, so O moves by at
+        most 2^-8 * sum_j w_j |V_j| -- ``wabs``, the attention of |V| with the
+        same weights, computed by the oracle.  When two large V rows of
+        opposite sign nearly cancel, this exceeds 4e-3 while |O| is small.
+    """
     if dt != "bf16":
         return TOL[dt]
     mag = np.abs(ref) if got is None else np.maximum(np.abs(ref), np.abs(got))
-    return TOL[dt] + bf16_half_ulp(mag)
+    tol = TOL[dt] + bf16_half_ulp(mag)
+    if wabs is not None:
+        tol = tol + 2.0 ** -8 * wabs
+    return tol
 
 
 def seeded(B, H, Nq, Nk, D, dt, seed):
