@@ -47,6 +47,8 @@
 //     LDS read (ds_read_b64_tr_b16): lane i of each 16-lane group receives 4
 //     keys of d = i when the group points at 4 keys x 4 groups of 4 columns.
 //   * LDS rows (128 bytes) have their 16-byte chunks XOR-swizzled by key.
+#include <type_traits>
+
 #include "fa2_device.h"
 #include "fa2_internal.h"
 
@@ -62,13 +64,13 @@ constexpr float kTau = 8.f;  // rescale threshold, base-2 units
 
 // Tuning knobs (compile-time).  FA2_KSWZ selects the K-tile chunk swizzle:
 // 1 = chunk ^ ((key/2) % 8), conflict-free for 16 lanes x 16 bytes over 64
-// banks; 0 = chunk ^ (key % 8).  FA2_SCHED = 1 interleaves the next block's
-// score MFMAs with the current block's softmax explicitly.
+// banks; 0 = chunk ^ (key % 8).  FA2_SGB = 1 pins the issue order inside a tile
+// (score MFMAs interleaved with the exponentials) with scheduling barriers.
 #ifndef FA2_KSWZ
 #define FA2_KSWZ 1
 #endif
-#ifndef FA2_SCHED
-#define FA2_SCHED 0
+#ifndef FA2_SGB
+#define FA2_SGB 1
 #endif
 
 __device__ __forceinline__ int kswz(int key) { return FA2_KSWZ ? (key >> 1) & 7 : key & 7; }
@@ -101,13 +103,16 @@ struct MfmaT<2> {
     }
 };
 
-template <int DT, bool CAUSAL>
+template <int DT, bool CAUSAL, bool WLSE>
 __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
     int Nq, int Nk, float scale_log2, int n_qtiles, int n_tiles) {
-    // Two K and two V buffers, as separate arrays (not one indexed array) so
-    // the compiler can see that reads of one never alias DMA into another.
+    // Two K and two V buffers of 64 rows, as separate arrays (not one indexed
+    // array) so the compiler can see that reads of one never alias DMA into
+    // another.  V buffer b holds keys [64b, 64b + 64) of its block; K buffer b
+    // holds keys [64b + 32, 64b + 96), one 32-key tile later, because the
+    // scores of tile t + 1 are computed while tile t is consumed.
     __shared__ __attribute__((aligned(16))) uint16_t sK0[kBC * kD];
     __shared__ __attribute__((aligned(16))) uint16_t sK1[kBC * kD];
     __shared__ __attribute__((aligned(16))) uint16_t sV0[kBC * kD];
@@ -143,7 +148,9 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
     for (int dc = 0; dc < 4; ++dc) qf[dc] = load16(rq, (uint32_t)((myq * kD + 16 * dc + 8 * h) * 2));
 
     const int kend = CAUSAL ? min(Nk, q0 + kBR) : Nk;
-    const int nblk = (kend + kBC - 1) / kBC;
+    const int nblk = (kend + kBC - 1) / kBC;  // 64-key V blocks
+    // Last 32-key tile this wave needs (causal: the one holding its diagonal).
+    const int t_last = CAUSAL ? min((kend + 31) / 32 - 1, qw / 32) : 2 * nblk - 1;
 
     // Rows past Nk are never loaded with data; make sure the V rows they
     // would occupy hold zeros (0 * V must stay 0 for the masked keys).
@@ -157,24 +164,25 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
         __syncthreads();
     }
 
-    // HBM/L2 -> LDS: wave w moves 16-byte units [(2w+i)*64, +64) of the
-    // block; unit P holds chunk (P%8) ^ swizzle(key) of key P/8 (swizzle kswz
-    // for K, key % 8 for V).
+    // HBM/L2 -> LDS of the 64 rows starting at key k0: wave w moves 16-byte
+    // units [(2w+i)*64, +64) of the block; unit P holds chunk (P%8) ^
+    // swizzle(row) of row P/8 (kswz for K, row % 8 for V).  Rows before key 0
+    // or past Nk are out of the descriptor's range and load nothing.
     auto dma = [&](const __amdgpu_buffer_rsrc_t &r, uint16_t *dst, int k0, bool r_is_k) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int unit = (2 * wave + i) * 64 + lane;
-            const int key = unit >> 3;
-            const int ch = (unit & 7) ^ (r_is_k ? kswz(key) : (key & 7));
-            const uint32_t off = (uint32_t)(((k0 + key) * kD + ch * 8) * 2);
+            const int row = unit >> 3;
+            const int ch = (unit & 7) ^ (r_is_k ? kswz(row) : (row & 7));
+            const int key = k0 + row;
+            const uint32_t off = key < 0 ? 0xFFFFFFF0u : (uint32_t)((key * kD + ch * 8) * 2);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (2 * wave + i) * 512), 16,
                                                      off, 0, 0, 0);
         }
     };
 
-    // LDS offsets that do not change from block to block.  Every key a lane
-    // reads sits at a multiple of 8 from its first one, so the chunk swizzle
-    // (key % 8) is fixed per lane and the rest is an immediate offset.
+    // LDS offsets that do not change from tile to tile (relative to the
+    // tile's first row; both halves of a 64-row buffer share the swizzle).
     int kofs[4], vofs[2];
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) kofs[dc] = ql * kD + (((2 * dc + h) ^ kswz(ql)) << 3);
@@ -188,19 +196,6 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
         }
     }
 
-    auto scores = [&](const uint16_t *kb, f32x16 *s) {
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[T][i] = 0.f;
-#pragma unroll
-            for (int dc = 0; dc < 4; ++dc) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(&kb[kofs[dc] + 32 * T * kD]);
-                s[T] = MfmaT<DT>::mma(a, qf[dc], s[T]);
-            }
-        }
-    };
-
     float m = -INFINITY;  // max used for the exponentials, base-2 units
     float l = 0.f;        // this lane's half of the running denominator (f32 P)
     float lt = 0.f;       // the same over P as rounded for the MFMA
@@ -212,127 +207,168 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
         oacc[1][i] = 0.f;
     }
 
-    // Block j's K lives in sK[j % 2] and its V in sV[j % 2].  While block b is
-    // computed, K_{b+2} and V_{b+1} stream in; they are waited for at the end
-    // of block b.
-    // Prologue: K_0, V_0, K_1 in and visible; scores of block 0.
-    dma(rk, sK0, 0, true);
-    dma(rv, sV0, 0, false);
-    if (nblk > 1) dma(rk, sK1, kBC, true);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    f32x16 sa[2], sb[2];
-    scores(sK0, sa);
-
-    // One block: on entry LDS holds K_{b+1} in kn and V_b in vc.  K_{b+2}
-    // goes to kd (K_b's buffer) and V_{b+1} to vd (V_{b-1}'s), both last read
-    // in the previous block.  scur holds the scores of block b; those of
-    // block b+1 go to snext.
-    auto step = [&](int b, const uint16_t *kn, uint16_t *kd, const uint16_t *vc, uint16_t *vd,
-                    f32x16 *scur, f32x16 *snext) {
-        const int k0 = b * kBC;
-        if (b + 1 < nblk) dma(rv, vd, k0 + kBC, false);
-        if (b + 2 < nblk) dma(rk, kd, k0 + 2 * kBC, true);
-
-        // Without a causal mask every block is live for every wave, and the
-        // scores of the next block are computed unconditionally (past the last
-        // block they read a stale buffer and are never used) so that they share
-        // one basic block with this block's softmax and P V and can interleave.
-        const bool next_live = CAUSAL ? (b + 1 < nblk && k0 + kBC <= qw + 31) : true;
-        const bool live = !(CAUSAL && k0 > qw + 31);
-        if (live) {
-            // scur[T][r] = S[myq][k0 + 32T + 8(r/4) + 4h + r%4]
-            const bool need_mask = (k0 + kBC > Nk) || (CAUSAL && k0 + kBC - 1 > qw);
-            if (need_mask) {
+    // One 32-key tile t.  On entry scur holds S^T of tile t (lane: query
+    // myq, register r: key 32t + 8(r/4) + 4h + r%4), kn points at the LDS
+    // rows of tile t+1's keys and vt at those of tile t's values.  With NEXT,
+    // the scores of tile t+1 go to snext; the matrix cores run them while the
+    // vector ALUs compute this tile's exponentials.
+    auto tile = [&](const int t, const uint16_t *kn, const uint16_t *vt, f32x16 &scur,
+                    f32x16 &snext, auto next_tag) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+        const int k0 = 32 * t;
+        // All LDS operands of this tile, issued first so their latency is
+        // covered by the max and the exponentials.
+        u32x4 kf[4];
+        if constexpr (NEXT) {
 #pragma unroll
-                for (int T = 0; T < 2; ++T)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
-                        bool ok = key < Nk;
-                        if (CAUSAL) ok = ok && key <= myq;
-                        if (!ok) scur[T][r] = -INFINITY;
-                    }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int T = 0; T < 2; ++T)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[T][r]);
-            mx = max_halves(mx) * scale_log2;
-            if (__builtin_amdgcn_ballot_w64(mx > m + kTau) != 0) {
-                const float m_new = fmaxf(m, mx);
-                const float corr = exp2f_fast(m - (m_new == -INFINITY ? 0.f : m_new));
-                l *= corr;
-                lt *= corr;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    oacc[0][i] *= corr;
-                    oacc[1][i] *= corr;
-                }
-                m = m_new;
-            }
-            if (next_live) scores(kn, snext);
-            const float m_use = m == -INFINITY ? 0.f : m;
-            float psum = 0.f;
-#pragma unroll
-            for (int T = 0; T < 2; ++T)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    u32x4 pk;
-#pragma unroll
-                    for (int r = 8 * c; r < 8 * c + 8; r += 2) {
-                        const float p0 = exp2f_fast(__builtin_fmaf(scur[T][r], scale_log2, -m_use));
-                        const float p1 = exp2f_fast(__builtin_fmaf(scur[T][r + 1], scale_log2, -m_use));
-                        const uint32_t w = pack2<DT>(p0, p1);
-                        pk[(r & 7) >> 1] = w;
-                        psum += p0 + p1;
-                        lt = dot2<DT>(w, ones, lt);
-                    }
-#pragma unroll
-                    for (int dt = 0; dt < 2; ++dt) {
-                        const uint16_t *src = vc + vofs[dt] + (32 * T + 16 * c) * kD;
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
-                        const s16x4 hi =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 8 * kD));
-                        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-                        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-                        const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
-                        oacc[dt] = MfmaT<DT>::mma(a, pk, oacc[dt]);
-                    }
-                }
-            l += psum;
-#if FA2_SCHED
-            // 8 K reads, then score MFMAs each followed by VALU work, then the
-            // V reads and the P V MFMAs likewise interleaved with VALU.
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-            }
-#endif
+            for (int dc = 0; dc < 4; ++dc) kf[dc] = *reinterpret_cast<const u32x4 *>(&kn[kofs[dc]]);
         }
+        u32x4 vf[2][2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                const uint16_t *src = vt + vofs[dt] + 16 * c * kD;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 8 * kD));
+                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+                const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+                vf[c][dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+            }
+
+        const bool need_mask = (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
+        if (need_mask) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                bool ok = key < Nk;
+                if (CAUSAL) ok = ok && key <= myq;
+                if (!ok) scur[r] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[r]);
+        mx = max_halves(mx) * scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > m + kTau) != 0) {
+            const float m_new = fmaxf(m, mx);
+            const float corr = exp2f_fast(m - (m_new == -INFINITY ? 0.f : m_new));
+            l *= corr;
+            lt *= corr;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                oacc[0][i] *= corr;
+                oacc[1][i] *= corr;
+            }
+            m = m_new;
+        }
+        const float m_use = m == -INFINITY ? 0.f : m;
+
+        if constexpr (NEXT) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) snext[i] = 0.f;
+        }
+        float ps[2] = {0.f, 0.f}, lp[2] = {0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            u32x4 pk;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 8 * c + 2 * j;
+                const float p0 = exp2f_fast(__builtin_fmaf(scur[r], scale_log2, -m_use));
+                const float p1 = exp2f_fast(__builtin_fmaf(scur[r + 1], scale_log2, -m_use));
+                const uint32_t w = pack2<DT>(p0, p1);
+                pk[j] = w;
+                if constexpr (WLSE) ps[j & 1] += p0 + p1;
+                lp[j & 1] = dot2<DT>(w, ones, lp[j & 1]);
+                if constexpr (NEXT) {
+                    // scores of the next tile, one MFMA per exponential pair of chunk 0
+                    if (c == 0) snext = MfmaT<DT>::mma(kf[j], qf[j], snext);
+                }
+            }
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) oacc[dt] = MfmaT<DT>::mma(vf[c][dt], pk, oacc[dt]);
+        }
+        lt += lp[0] + lp[1];
+        if constexpr (WLSE) l += ps[0] + ps[1];
+#if FA2_SGB
+        // Issue order inside the tile: each score MFMA followed by the
+        // vector work of one exponential pair, then P V chunk 0, the
+        // exponentials of chunk 1, P V chunk 1.
+        if constexpr (NEXT) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, WLSE ? 8 : 6, 0);
+            }
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x002, WLSE ? 32 : 24, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, WLSE ? 16 : 12, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, WLSE ? 16 : 12, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#endif
+    };
+
+    auto run_tile = [&](const int t, const uint16_t *kn, const uint16_t *vt, f32x16 &scur,
+                        f32x16 &snext) {
+        if constexpr (CAUSAL) {
+            if (t > t_last) return;
+            if (t + 1 <= t_last)
+                tile(t, kn, vt, scur, snext, std::true_type{});
+            else
+                tile(t, kn, vt, scur, snext, std::false_type{});
+        } else {
+            tile(t, kn, vt, scur, snext, std::true_type{});
+        }
+    };
+
+    // One 64-key V block b (tiles 2b, 2b+1).  On entry V block b is in vc and
+    // K buffer kc holds keys [64b + 32, 64b + 96) (tiles 2b+1 and 2b+2);
+    // block b+1 streams into vd / kd, last read in block b-1.
+    auto block = [&](int b, const uint16_t *kc, uint16_t *kd, const uint16_t *vc, uint16_t *vd,
+                     f32x16 &sa, f32x16 &sb) {
+        if (b + 1 < nblk) {
+            dma(rv, vd, (b + 1) * kBC, false);
+            dma(rk, kd, (b + 1) * kBC + 32, true);
+        }
+        run_tile(2 * b, kc, vc, sa, sb);
+        run_tile(2 * b + 1, kc + 32 * kD, vc + 32 * kD, sb, sa);
         // This block's DMA has landed; after the barrier every wave's has.
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
     };
 
+    // Prologue: V block 0, K buffer 0 (keys 32..95) and, in K buffer 1's upper
+    // half, keys 0..31; the scores of tile 0; then a barrier so that K
+    // buffer 1 may be refilled.
+    dma(rv, sV0, 0, false);
+    dma(rk, sK0, 32, true);
+    dma(rk, sK1, -32, true);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 sa, sb;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sa[i] = 0.f;
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(&sK1[32 * kD + kofs[dc]]);
+        sa = MfmaT<DT>::mma(a, qf[dc], sa);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
     // Unrolled by 2 so every buffer and register choice is fixed at compile time.
     for (int b = 0; b < nblk; b += 2) {
-        step(b, sK1, sK0, sV0, sV1, sa, sb);
-        if (b + 1 < nblk) step(b + 1, sK0, sK1, sV1, sV0, sb, sa);
+        block(b, sK0, sK1, sV0, sV1, sa, sb);
+        if (b + 1 < nblk) block(b + 1, sK1, sK0, sV1, sV0, sa, sb);
     }
 
-    // oacc[dt][r] = O[myq][32dt + 8(r/4) + 4h + r%4] * l
-    l += __shfl_xor(l, 32);
+    // oacc[dt][r] = O[myq][32dt + 8(r/4) + 4h + r%4] * lt
     lt += __shfl_xor(lt, 32);
+    if constexpr (WLSE) l += __shfl_xor(l, 32);
     if (myq < Nq) {
         const float inv = 1.f / lt;
         uint16_t *orow = O + ((size_t)bh * Nq + myq) * kD;
@@ -347,8 +383,18 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
                 w[1] = pack2<DT>(oacc[dt][r + 2] * inv, oacc[dt][r + 3] * inv);
                 *reinterpret_cast<u32x2 *>(orow + d) = w;
             }
-        if (LSE && h == 0) LSE[(size_t)bh * Nq + myq] = (m + log2f_fast(l)) * kLn2;
+        if constexpr (WLSE) {
+            if (h == 0) LSE[(size_t)bh * Nq + myq] = (m + log2f_fast(l)) * kLn2;
+        }
     }
+}
+
+template <int DT, bool CAUSAL, bool WLSE>
+fa2_status launch_v(const FwdArgs &a, int n_qtiles, int n_tiles, hipStream_t st) {
+    return launch(fwd_mfma_d64_kernel<DT, CAUSAL, WLSE>, dim3((unsigned)n_tiles),
+                  dim3(kWaves * 64), st, (const uint16_t *)a.q, (const uint16_t *)a.k,
+                  (const uint16_t *)a.v, (uint16_t *)a.o, a.lse, a.Nq, a.Nk,
+                  a.scale * kLog2e, n_qtiles, n_tiles);
 }
 
 template <int DT>
@@ -356,16 +402,12 @@ fa2_status launch_dt(const FwdArgs &a, hipStream_t st) {
     const int n_qtiles = (a.Nq + kBR - 1) / kBR;
     const long long n_tiles = (long long)n_qtiles * a.B * a.H;
     if (n_tiles > 0x7FFFFFFF) return FA2_ERR_UNSUPPORTED;
-    const dim3 grid((unsigned)n_tiles);
-    const dim3 block(kWaves * 64);
-    const float sl2 = a.scale * kLog2e;
+    const int nt = (int)n_tiles;
     if (a.causal)
-        return launch(fwd_mfma_d64_kernel<DT, true>, grid, block, st, (const uint16_t *)a.q,
-                      (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o, a.lse, a.Nq,
-                      a.Nk, sl2, n_qtiles, (int)n_tiles);
-    return launch(fwd_mfma_d64_kernel<DT, false>, grid, block, st, (const uint16_t *)a.q,
-                  (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o, a.lse, a.Nq,
-                  a.Nk, sl2, n_qtiles, (int)n_tiles);
+        return a.lse ? launch_v<DT, true, true>(a, n_qtiles, nt, st)
+                     : launch_v<DT, true, false>(a, n_qtiles, nt, st);
+    return a.lse ? launch_v<DT, false, true>(a, n_qtiles, nt, st)
+                 : launch_v<DT, false, false>(a, n_qtiles, nt, st);
 }
 
 }  // namespace

@@ -16,11 +16,17 @@ pytestmark = pytest.mark.gpu
 
 
 def run_fwd(q, k, v, dt, scale, causal, lse=True):
+    """Run attn_fwd; with ``lse`` also run it without the LSE output (the
+    kernels then skip the float32 row sum) and require the same O bit for
+    bit."""
     tq, tk, tv = upload(q, dt), upload(k, dt), upload(v, dt)
     out = fa2.attn_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=lse)
     import torch
     torch.cuda.synchronize()
     if lse:
+        o_only = fa2.attn_fwd(tq, tk, tv, scale=scale, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o_only, out[0]), "O differs between the runs with and without LSE"
         return download_f64(out[0]), download_f64(out[1])
     return download_f64(out), None
 
