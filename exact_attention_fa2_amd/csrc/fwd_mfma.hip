@@ -60,7 +60,10 @@ constexpr int kD = 64;
 constexpr int kBR = 128;     // query rows per workgroup
 constexpr int kBC = 64;      // keys per block
 constexpr int kWaves = 4;    // 32 query rows per wave
-constexpr float kTau = 8.f;  // rescale threshold, base-2 units
+// A tile is accepted with the current running max when each lane's sum of its
+// 16 rounded P values is at most this (so every P <= 2^8, far below the f16
+// and bf16 overflow); otherwise the max is taken and O rescaled.
+constexpr float kLazyCap = 256.f;
 
 // Tuning knobs (compile-time).  FA2_KSWZ selects the K-tile chunk swizzle:
 // 1 = chunk ^ ((key/2) % 8), conflict-free for 16 lanes x 16 bytes over 64
@@ -246,13 +249,53 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
                 if (!ok) scur[r] = -INFINITY;
             }
         }
-        float mx = -INFINITY;
+        // P = exp2(S*scale*log2e - m) for this tile, rounded for the MFMA
+        // (pk), with its row sums (lp from the rounded P, ps from f32 P).
+        u32x4 pk[2];
+        float ps[2], lp[2];
+        auto exps = [&](float m_use, bool with_next) __attribute__((always_inline)) {
+            ps[0] = ps[1] = lp[0] = lp[1] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[r]);
-        mx = max_halves(mx) * scale_log2;
-        if (__builtin_amdgcn_ballot_w64(mx > m + kTau) != 0) {
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 8 * c + 2 * j;
+                    const float p0 = exp2f_fast(__builtin_fmaf(scur[r], scale_log2, -m_use));
+                    const float p1 = exp2f_fast(__builtin_fmaf(scur[r + 1], scale_log2, -m_use));
+                    const uint32_t w = pack2<DT>(p0, p1);
+                    pk[c][j] = w;
+                    if constexpr (WLSE) ps[j & 1] += p0 + p1;
+                    lp[j & 1] = dot2<DT>(w, ones, lp[j & 1]);
+                    if constexpr (NEXT) {
+                        // scores of the next tile, one MFMA per exponential pair of chunk 0
+                        if (with_next && c == 0) snext = MfmaT<DT>::mma(kf[j], qf[j], j == 0 ? f32x16{} : snext);
+                    }
+                }
+        };
+        // The running max m is only moved when it must be ("Flash Attention",
+        // FlashAttention 4: conditional rescaling).  First try the current m:
+        // if every lane's sum of this tile's rounded P is at most 2^8, every P
+        // is, and the tile is done without computing its max.  Otherwise (and
+        // on a row's first tile, where m is still -inf) take the max, rescale
+        // O and the sums, and redo the exponentials.
+        exps(m == -INFINITY ? 0.f : m, true);
+#if FA2_SGB
+        if constexpr (NEXT) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x002, WLSE ? 8 : 6, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+        }
+#endif
+        if (__builtin_amdgcn_ballot_w64(m == -INFINITY || lp[0] + lp[1] > kLazyCap) != 0) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[r]);
+            mx = max_halves(mx) * scale_log2;
             const float m_new = fmaxf(m, mx);
-            const float corr = exp2f_fast(m - (m_new == -INFINITY ? 0.f : m_new));
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float corr = exp2f_fast(m - m_use);
             l *= corr;
             lt *= corr;
 #pragma unroll
@@ -261,55 +304,14 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
                 oacc[1][i] *= corr;
             }
             m = m_new;
+            exps(m_use, false);
         }
-        const float m_use = m == -INFINITY ? 0.f : m;
-
-        if constexpr (NEXT) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) snext[i] = 0.f;
-        }
-        float ps[2] = {0.f, 0.f}, lp[2] = {0.f, 0.f};
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            u32x4 pk;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 8 * c + 2 * j;
-                const float p0 = exp2f_fast(__builtin_fmaf(scur[r], scale_log2, -m_use));
-                const float p1 = exp2f_fast(__builtin_fmaf(scur[r + 1], scale_log2, -m_use));
-                const uint32_t w = pack2<DT>(p0, p1);
-                pk[j] = w;
-                if constexpr (WLSE) ps[j & 1] += p0 + p1;
-                lp[j & 1] = dot2<DT>(w, ones, lp[j & 1]);
-                if constexpr (NEXT) {
-                    // scores of the next tile, one MFMA per exponential pair of chunk 0
-                    if (c == 0) snext = MfmaT<DT>::mma(kf[j], qf[j], snext);
-                }
-            }
-#pragma unroll
-            for (int dt = 0; dt < 2; ++dt) oacc[dt] = MfmaT<DT>::mma(vf[c][dt], pk, oacc[dt]);
-        }
+            for (int dt = 0; dt < 2; ++dt) oacc[dt] = MfmaT<DT>::mma(vf[c][dt], pk[c], oacc[dt]);
         lt += lp[0] + lp[1];
         if constexpr (WLSE) l += ps[0] + ps[1];
-#if FA2_SGB
-        // Issue order inside the tile: each score MFMA followed by the
-        // vector work of one exponential pair, then P V chunk 0, the
-        // exponentials of chunk 1, P V chunk 1.
-        if constexpr (NEXT) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, WLSE ? 8 : 6, 0);
-            }
-        } else {
-            __builtin_amdgcn_sched_group_barrier(0x002, WLSE ? 32 : 24, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, WLSE ? 16 : 12, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, WLSE ? 16 : 12, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-#endif
     };
 
     auto run_tile = [&](const int t, const uint16_t *kn, const uint16_t *vt, f32x16 &scur,
