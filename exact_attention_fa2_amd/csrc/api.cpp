@@ -91,11 +91,13 @@ FA2_API fa2_status attn_fwd_ws(const void *q, const void *k, const void *v, void
 
 FA2_API size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int causal,
                                        fa2_dtype dtype) {
-    (void)causal;
-    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D != 64 || dtype != FA2_F32) return 0;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D != 64 || !valid_dtype(dtype)) return 0;
+    if (causal && Nq != Nk) return 0;
+    if ((long long)B * H > 65535) return 0;
     int cus = 256;
     if (const DeviceInfo *dev = current_device()) cus = dev->num_cus;
-    return fa2::f32_workspace_bytes(B, H, Nq, Nk, cus);
+    if (dtype == FA2_F32) return fa2::f32_workspace_bytes(B, H, Nq, Nk, cus);
+    return fa2::mfma_workspace_bytes(B, H, Nq, Nk, causal, cus);
 }
 
 FA2_API fa2_status attn_decode_split(const void *q, const void *k, const void *v,

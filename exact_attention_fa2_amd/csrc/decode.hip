@@ -14,7 +14,9 @@
 // before writing one unnormalised partial (O_s, m_s, l_s).
 //
 // Combine kernel: one workgroup per (b,h), one thread per output column;
-// weights exp(m_s - m_g), a single division by l_g at the end.
+// weights exp(m_s - m_g), a single division by l_g at the end.  It also
+// merges the key-split partials of the forward kernels (one workgroup per
+// query row); those may carry a second denominator for the LSE.
 #include "fa2_device.h"
 #include "fa2_internal.h"
 
@@ -175,6 +177,7 @@ template <int DT, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(const float *__restrict__ o_part,
                                                            const float *__restrict__ m_part,
                                                            const float *__restrict__ l_part,
+                                                           const float *__restrict__ l2_part,
                                                            void *__restrict__ O,
                                                            float *__restrict__ LSE, int n_splits) {
     const size_t bh = blockIdx.x;  // one output row (a (b,h) pair for decode)
@@ -183,12 +186,15 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float *__restri
     const float *lp = l_part + bh * n_splits;
     const float *op = o_part + bh * n_splits * D;
     float mg = -INFINITY;
+#pragma unroll 8
     for (int s = 0; s < n_splits; ++s) mg = fmaxf(mg, mp[s]);
-    float lg = 0.f, acc = 0.f;
+    float lg = 0.f, lg2 = 0.f, acc = 0.f;
+#pragma unroll 8
     for (int s = 0; s < n_splits; ++s) {
         const float ms = mp[s];
         const float wt = ms == -INFINITY ? 0.f : exp2f_fast((ms - mg) * kLog2e);
         lg += wt * lp[s];
+        if (l2_part) lg2 += wt * l2_part[bh * n_splits + s];
         acc += wt * op[(size_t)s * D + d];
     }
     const float o = acc / lg;
@@ -198,7 +204,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float *__restri
         const uint32_t w = pack2<DT>(o, 0.f);
         ((uint16_t *)O)[bh * D + d] = (uint16_t)(w & 0xFFFF);
     }
-    if (LSE && d == 0) LSE[bh] = mg + log2f_fast(lg) * kLn2;
+    if (LSE && d == 0) LSE[bh] = mg + log2f_fast(l2_part ? lg2 : lg) * kLn2;
 }
 
 template <int DT, int D>
@@ -210,14 +216,14 @@ fa2_status split_dt(const DecodeArgs &a, hipStream_t st) {
 }
 
 template <int DT>
-fa2_status combine_dt(const float *op, const float *mp, const float *lp, void *o, float *lse,
-                      size_t rows, int D, int ns, hipStream_t st) {
+fa2_status combine_dt(const float *op, const float *mp, const float *lp, const float *lp2, void *o,
+                      float *lse, size_t rows, int D, int ns, hipStream_t st) {
     if (rows > 0x7FFFFFFF) return FA2_ERR_UNSUPPORTED;
     if (D == 64)
         return launch(decode_combine_kernel<DT, 64>, dim3((unsigned)rows), dim3(64), st, op, mp, lp,
-                      o, lse, ns);
+                      lp2, o, lse, ns);
     return launch(decode_combine_kernel<DT, 128>, dim3((unsigned)rows), dim3(128), st, op, mp, lp,
-                  o, lse, ns);
+                  lp2, o, lse, ns);
 }
 
 }  // namespace
@@ -235,10 +241,12 @@ fa2_status launch_decode_split(const DecodeArgs &a, fa2_dtype dt, hipStream_t st
 
 fa2_status launch_combine_rows(const float *o_part, const float *m_part, const float *l_part,
                                void *o, float *lse, size_t rows, int D, int n_splits, fa2_dtype dt,
-                               hipStream_t st) {
-    if (dt == FA2_F32) return combine_dt<0>(o_part, m_part, l_part, o, lse, rows, D, n_splits, st);
-    if (dt == FA2_F16) return combine_dt<1>(o_part, m_part, l_part, o, lse, rows, D, n_splits, st);
-    return combine_dt<2>(o_part, m_part, l_part, o, lse, rows, D, n_splits, st);
+                               hipStream_t st, const float *l2_part) {
+    if (dt == FA2_F32)
+        return combine_dt<0>(o_part, m_part, l_part, l2_part, o, lse, rows, D, n_splits, st);
+    if (dt == FA2_F16)
+        return combine_dt<1>(o_part, m_part, l_part, l2_part, o, lse, rows, D, n_splits, st);
+    return combine_dt<2>(o_part, m_part, l_part, l2_part, o, lse, rows, D, n_splits, st);
 }
 
 fa2_status launch_decode_combine(const float *o_part, const float *m_part, const float *l_part,

@@ -30,6 +30,7 @@ struct FwdArgs {
 fa2_status launch_fwd_f32_d64(const FwdArgs &a, hipStream_t st);
 size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int num_cus);
 fa2_status launch_fwd_mfma_d64(const FwdArgs &a, fa2_dtype dt, hipStream_t st);
+size_t mfma_workspace_bytes(int B, int H, int Nq, int Nk, int causal, int num_cus);
 
 struct DecodeArgs {
     const void *q, *k, *v;
@@ -41,10 +42,11 @@ struct DecodeArgs {
 
 fa2_status launch_decode_split(const DecodeArgs &a, fa2_dtype dt, hipStream_t st);
 // Merge per-row partials [rows][n_splits][D] (natural-log m) into o [rows][D]
-// of dtype dt and, if lse is not null, lse [rows].
+// of dtype dt and, if lse is not null, lse [rows].  O is divided by the merged
+// l_part; the LSE uses the merged l2_part when it is given, else l_part.
 fa2_status launch_combine_rows(const float *o_part, const float *m_part, const float *l_part,
                                void *o, float *lse, size_t rows, int D, int n_splits, fa2_dtype dt,
-                               hipStream_t st);
+                               hipStream_t st, const float *l2_part = nullptr);
 fa2_status launch_decode_combine(const float *o_part, const float *m_part, const float *l_part,
                                  void *o, int B, int H, int D, int n_splits, fa2_dtype dt,
                                  hipStream_t st);

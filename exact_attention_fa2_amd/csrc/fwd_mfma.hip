@@ -47,6 +47,7 @@
 //     LDS read (ds_read_b64_tr_b16): lane i of each 16-lane group receives 4
 //     keys of d = i when the group points at 4 keys x 4 groups of 4 columns.
 //   * LDS rows (128 bytes) have their 16-byte chunks XOR-swizzled by key.
+#include <algorithm>
 #include <type_traits>
 
 #include "fa2_device.h"
@@ -106,11 +107,18 @@ struct MfmaT<2> {
     }
 };
 
-template <int DT, bool CAUSAL, bool WLSE>
+// SPLIT: the key blocks of each query tile are cut into gridDim.y chunks, one
+// per workgroup along y ("Flash decoding": split the keys, keep unnormalised
+// partials); the workgroup writes, per row and chunk, O_s (not divided),
+// m_s (natural-log units), the denominator of the rounded P (lt, which
+// normalises O) and, with WLSE, that of the f32 P (l, for the LSE), and the
+// combine kernel merges them.
+template <int DT, bool CAUSAL, bool WLSE, bool SPLIT>
 __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
-    int Nq, int Nk, float scale_log2, int n_qtiles, int n_tiles) {
+    float *__restrict__ o_part, float *__restrict__ m_part, float *__restrict__ l_part,
+    float *__restrict__ l2_part, int Nq, int Nk, float scale_log2, int n_qtiles, int n_tiles) {
     // Two K and two V buffers of 64 rows, as separate arrays (not one indexed
     // array) so the compiler can see that reads of one never alias DMA into
     // another.  V buffer b holds keys [64b, 64b + 64) of its block; K buffer b
@@ -151,7 +159,14 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
     for (int dc = 0; dc < 4; ++dc) qf[dc] = load16(rq, (uint32_t)((myq * kD + 16 * dc + 8 * h) * 2));
 
     const int kend = CAUSAL ? min(Nk, q0 + kBR) : Nk;
-    const int nblk = (kend + kBC - 1) / kBC;  // 64-key V blocks
+    const int nblk = (kend + kBC - 1) / kBC;  // 64-key V blocks of this query tile
+    // This workgroup's blocks [b0, b1): all of them, or its chunk of them.
+    int b0 = 0, b1 = nblk;
+    if constexpr (SPLIT) {
+        const int nb = (nblk + (int)gridDim.y - 1) / (int)gridDim.y;
+        b0 = min(nblk, (int)blockIdx.y * nb);
+        b1 = min(nblk, b0 + nb);
+    }
     // Last 32-key tile this wave needs (causal: the one holding its diagonal).
     const int t_last = CAUSAL ? min((kend + 31) / 32 - 1, qw / 32) : 2 * nblk - 1;
 
@@ -332,7 +347,7 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
     // block b+1 streams into vd / kd, last read in block b-1.
     auto block = [&](int b, const uint16_t *kc, uint16_t *kd, const uint16_t *vc, uint16_t *vd,
                      f32x16 &sa, f32x16 &sb) {
-        if (b + 1 < nblk) {
+        if (b + 1 < b1) {
             dma(rv, vd, (b + 1) * kBC, false);
             dma(rk, kd, (b + 1) * kBC + 32, true);
         }
@@ -343,34 +358,71 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
         __builtin_amdgcn_s_barrier();
     };
 
-    // Prologue: V block 0, K buffer 0 (keys 32..95) and, in K buffer 1's upper
-    // half, keys 0..31; the scores of tile 0; then a barrier so that K
-    // buffer 1 may be refilled.
-    dma(rv, sV0, 0, false);
-    dma(rk, sK0, 32, true);
-    dma(rk, sK1, -32, true);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    f32x16 sa, sb;
+    // Prologue: V block b0, K buffer 0 (keys 64 b0 + 32 .. + 95) and, in K
+    // buffer 1's upper half, keys 64 b0 .. + 31; the scores of tile 2 b0; then
+    // a barrier so that K buffer 1 may be refilled.  (b0 and b1 are the same
+    // for every wave, so all of them take the same branches to the barriers.)
+    if (b0 < b1) {
+        dma(rv, sV0, b0 * kBC, false);
+        dma(rk, sK0, b0 * kBC + 32, true);
+        dma(rk, sK1, b0 * kBC - 32, true);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        f32x16 sa, sb;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sa[i] = 0.f;
+        for (int i = 0; i < 16; ++i) sa[i] = 0.f;
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(&sK1[32 * kD + kofs[dc]]);
-        sa = MfmaT<DT>::mma(a, qf[dc], sa);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+        for (int dc = 0; dc < 4; ++dc) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(&sK1[32 * kD + kofs[dc]]);
+            sa = MfmaT<DT>::mma(a, qf[dc], sa);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
 
-    // Unrolled by 2 so every buffer and register choice is fixed at compile time.
-    for (int b = 0; b < nblk; b += 2) {
-        block(b, sK0, sK1, sV0, sV1, sa, sb);
-        if (b + 1 < nblk) block(b + 1, sK1, sK0, sV1, sV0, sa, sb);
+        // Unrolled by 2 so every buffer and register choice is fixed at compile time.
+        for (int b = b0; b < b1; b += 2) {
+            block(b, sK0, sK1, sV0, sV1, sa, sb);
+            if (b + 1 < b1) block(b + 1, sK1, sK0, sV1, sV0, sa, sb);
+        }
     }
 
     // oacc[dt][r] = O[myq][32dt + 8(r/4) + 4h + r%4] * lt
     lt += __shfl_xor(lt, 32);
     if constexpr (WLSE) l += __shfl_xor(l, 32);
+    if constexpr (SPLIT) {
+        // Partials: stage this wave's 32 rows x 64 columns in LDS (each wave
+        // its own 8 KB buffer, free after the last barrier) so that each row's
+        // 256 bytes go out as one contiguous piece.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        float *stage = reinterpret_cast<float *>(wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int r = 4 * g4;
+                *reinterpret_cast<f32x4 *>(stage + ql * kD + ((32 * dt + 8 * g4 + 4 * h) ^ (4 * (ql & 7)))) =
+                    f32x4{oacc[dt][r], oacc[dt][r + 1], oacc[dt][r + 2], oacc[dt][r + 3]};
+            }
+        const size_t nch = gridDim.y;
+        if (myq < Nq && h == 0) {
+            const size_t pidx = ((size_t)bh * Nq + myq) * nch + blockIdx.y;
+            m_part[pidx] = m == -INFINITY ? -INFINITY : m * kLn2;  // natural-log units
+            l_part[pidx] = lt;
+            if constexpr (WLSE) l2_part[pidx] = l;
+        }
+        // lane i of each 16-lane group writes 16 bytes of row 4j + lane/16
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = 4 * j + (lane >> 4);
+            const int col = 4 * (lane & 15);
+            const int q = qw + row;
+            const f32x4 val = *reinterpret_cast<const f32x4 *>(stage + row * kD + (col ^ (4 * (row & 7))));
+            if (q < Nq)
+                *reinterpret_cast<f32x4 *>(o_part + (((size_t)bh * Nq + q) * nch + blockIdx.y) * kD + col) = val;
+        }
+        return;
+    }
     if (myq < Nq) {
         const float inv = 1.f / lt;
         uint16_t *orow = O + ((size_t)bh * Nq + myq) * kD;
@@ -391,31 +443,84 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
     }
 }
 
+struct Plan {
+    int n_qtiles, n_tiles, chunks;
+};
+
+#ifndef FA2_MFMA_SPLIT_WGS
+#define FA2_MFMA_SPLIT_WGS 2  // target workgroups per compute unit when splitting keys
+#endif
+#ifndef FA2_MFMA_SPLIT_BELOW
+#define FA2_MFMA_SPLIT_BELOW 8  // split only with at most num_cus / this many query tiles
+#endif
+
+// Split the keys of each query tile when the query tiles fill at most an
+// eighth of the compute units (with more, writing and merging the partials
+// costs more than the idle units), into at most one chunk per two key blocks.
+Plan plan(int B, int H, int Nq, int Nk, int num_cus) {
+    Plan p;
+    p.n_qtiles = (Nq + kBR - 1) / kBR;
+    const long long nt = (long long)p.n_qtiles * B * H;
+    p.n_tiles = nt > 0x7FFFFFFF ? -1 : (int)nt;
+    p.chunks = 1;
+    if (nt > 0 && nt * FA2_MFMA_SPLIT_BELOW <= num_cus) {
+        const long long nblk = (Nk + kBC - 1) / kBC;
+        long long c = ((long long)FA2_MFMA_SPLIT_WGS * num_cus + nt - 1) / nt;
+        c = std::min<long long>(c, std::max<long long>(1, nblk / 2));
+        p.chunks = (int)std::min<long long>(c, 32);
+    }
+    return p;
+}
+
+size_t part_bytes(const FwdArgs &a, int chunks) {
+    return (size_t)a.B * a.H * a.Nq * chunks * (kD + 3) * sizeof(float);
+}
+
 template <int DT, bool CAUSAL, bool WLSE>
-fa2_status launch_v(const FwdArgs &a, int n_qtiles, int n_tiles, hipStream_t st) {
-    return launch(fwd_mfma_d64_kernel<DT, CAUSAL, WLSE>, dim3((unsigned)n_tiles),
-                  dim3(kWaves * 64), st, (const uint16_t *)a.q, (const uint16_t *)a.k,
-                  (const uint16_t *)a.v, (uint16_t *)a.o, a.lse, a.Nq, a.Nk,
-                  a.scale * kLog2e, n_qtiles, n_tiles);
+fa2_status launch_v(const FwdArgs &a, const Plan &p, hipStream_t st) {
+    const uint16_t *q = (const uint16_t *)a.q, *k = (const uint16_t *)a.k, *v = (const uint16_t *)a.v;
+    const float sl2 = a.scale * kLog2e;
+    if (p.chunks > 1 && a.ws && a.ws_bytes >= part_bytes(a, p.chunks)) {
+        const size_t n = (size_t)a.B * a.H * a.Nq * p.chunks;
+        float *o_part = (float *)a.ws;
+        float *m_part = o_part + n * kD;
+        float *l_part = m_part + n;
+        float *l2_part = l_part + n;
+        fa2_status s = launch(fwd_mfma_d64_kernel<DT, CAUSAL, WLSE, true>,
+                              dim3((unsigned)p.n_tiles, (unsigned)p.chunks), dim3(kWaves * 64), st,
+                              q, k, v, (uint16_t *)a.o, a.lse, o_part, m_part, l_part, l2_part, a.Nq,
+                              a.Nk, sl2, p.n_qtiles, p.n_tiles);
+        if (s != FA2_OK) return s;
+        return launch_combine_rows(o_part, m_part, l_part, a.o, a.lse, (size_t)a.B * a.H * a.Nq, kD,
+                                   p.chunks, DT == 1 ? FA2_F16 : FA2_BF16, st,
+                                   WLSE ? l2_part : nullptr);
+    }
+    return launch(fwd_mfma_d64_kernel<DT, CAUSAL, WLSE, false>, dim3((unsigned)p.n_tiles),
+                  dim3(kWaves * 64), st, q, k, v, (uint16_t *)a.o, a.lse, (float *)nullptr,
+                  (float *)nullptr, (float *)nullptr, (float *)nullptr, a.Nq, a.Nk, sl2,
+                  p.n_qtiles, p.n_tiles);
 }
 
 template <int DT>
 fa2_status launch_dt(const FwdArgs &a, hipStream_t st) {
-    const int n_qtiles = (a.Nq + kBR - 1) / kBR;
-    const long long n_tiles = (long long)n_qtiles * a.B * a.H;
-    if (n_tiles > 0x7FFFFFFF) return FA2_ERR_UNSUPPORTED;
-    const int nt = (int)n_tiles;
+    const Plan p = plan(a.B, a.H, a.Nq, a.Nk, a.num_cus);
+    if (p.n_tiles < 0) return FA2_ERR_UNSUPPORTED;
     if (a.causal)
-        return a.lse ? launch_v<DT, true, true>(a, n_qtiles, nt, st)
-                     : launch_v<DT, true, false>(a, n_qtiles, nt, st);
-    return a.lse ? launch_v<DT, false, true>(a, n_qtiles, nt, st)
-                 : launch_v<DT, false, false>(a, n_qtiles, nt, st);
+        return a.lse ? launch_v<DT, true, true>(a, p, st) : launch_v<DT, true, false>(a, p, st);
+    return a.lse ? launch_v<DT, false, true>(a, p, st) : launch_v<DT, false, false>(a, p, st);
 }
 
 }  // namespace
 
 fa2_status launch_fwd_mfma_d64(const FwdArgs &a, fa2_dtype dt, hipStream_t st) {
     return dt == FA2_F16 ? launch_dt<1>(a, st) : launch_dt<2>(a, st);
+}
+
+size_t mfma_workspace_bytes(int B, int H, int Nq, int Nk, int causal, int num_cus) {
+    (void)causal;
+    const Plan p = plan(B, H, Nq, Nk, num_cus);
+    if (p.chunks <= 1) return 0;
+    return (size_t)B * H * Nq * p.chunks * (kD + 3) * sizeof(float);
 }
 
 }  // namespace fa2

@@ -98,9 +98,9 @@ def attn_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=
              stream=None, workspace=None, use_workspace=True):
     """Exact attention forward.  q [B,H,Nq,D], k/v [B,H,Nk,D] (same dtype).
 
-    When the library asks for a workspace for this shape (few rows: it then
-    splits the keys across workgroups), one is taken from ``workspace`` if
-    given and large enough, else allocated with torch for this call.
+    When the library asks for a workspace for this shape (few query tiles: it
+    then splits the keys across workgroups), one is taken from ``workspace``
+    if given and large enough, else allocated with torch for this call.
     ``use_workspace=False`` calls the plain attn_fwd entry point instead.
     Returns o (and lse [B,H,Nq] float32 when ``return_lse``)."""
     torch = _torch()

@@ -82,14 +82,16 @@ fa2_status attn_fwd(const void *q, const void *k, const void *v, void *o, float 
 /*
  * attn_fwd_ws -- attn_fwd with a caller-provided device workspace.
  *
- * Same result and arguments as attn_fwd.  When there are too few rows to fill
- * the device (few heads, few 64-row query groups), a workspace of at least
+ * Same result and arguments as attn_fwd.  When there are too few query tiles
+ * to fill the device (few heads, short sequences), a workspace of at least
  * attn_fwd_workspace_size() bytes lets the library split the keys of each
- * query group into chunks, compute one unnormalised partial (O_s, m_s, l_s)
- * per chunk and merge them with the flash-decoding combine ("Flash
+ * query tile into chunks, compute one unnormalised partial (O_s, m_s, l_s)
+ * per row and chunk and merge them with the flash-decoding combine ("Flash
  * decoding": Overview of the algorithm -- the split is the same, applied to
  * many query rows; "Flash Attention": the (m, l) monoid).  With a NULL or
- * smaller workspace it runs exactly as attn_fwd.
+ * smaller workspace it runs exactly as attn_fwd.  The two paths may differ in
+ * the last bits (the sums are grouped differently), each within the bounds
+ * stated for attn_fwd.
  *   workspace  device memory, 16-byte aligned, owned by the caller; its
  *              contents on entry are ignored and on return are unspecified.
  *              Calls that share one workspace must not overlap in time.
@@ -100,9 +102,9 @@ fa2_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, flo
 
 /*
  * attn_fwd_workspace_size -- bytes of workspace attn_fwd_ws would use for
- * this shape on the current device (0: it would not split).  Currently
- * nonzero only for dtype F32 with D == 64.  If the device cannot be queried it
- * assumes 256 compute units.
+ * this shape on the current device (0: it would not split, or the shape is
+ * not supported).  If the device cannot be queried it assumes 256 compute
+ * units.
  */
 size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int causal, fa2_dtype dtype);
 

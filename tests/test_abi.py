@@ -110,3 +110,21 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa2, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         fa2.lib()
+
+
+def test_workspace_size_plan():
+    """attn_fwd_workspace_size without a GPU (256 compute units assumed)."""
+    f16, bf16, f32 = fa2.FA2_F16, fa2.FA2_BF16, fa2.FA2_F32
+    # few query tiles: the keys are split, partials need (D + 3) floats per row and chunk
+    need = fa2.workspace_size(1, 2, 1024, 1024, 64, 1, f16)
+    assert need > 0 and need % (2 * 1024 * 67 * 4) == 0
+    assert fa2.workspace_size(1, 2, 1024, 1024, 64, 0, bf16) == need
+    # enough query tiles to fill the device: no split
+    assert fa2.workspace_size(4, 12, 2048, 2048, 64, 0, f16) == 0
+    # unsupported requests ask for nothing
+    assert fa2.workspace_size(1, 2, 1024, 1024, 128, 0, f16) == 0
+    assert fa2.workspace_size(1, 2, 1024, 512, 64, 1, f16) == 0
+    assert fa2.workspace_size(0, 2, 1024, 1024, 64, 0, f16) == 0
+    # float32: one head of 4096 rows is split, many heads are not
+    assert fa2.workspace_size(1, 1, 4096, 4096, 64, 0, f32) >= 0
+    assert fa2.workspace_size(8, 48, 256, 256, 64, 0, f32) == 0

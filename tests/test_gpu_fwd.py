@@ -213,6 +213,35 @@ def test_f32_schedules(shape, causal):
         assert_close("f32 schedule %s LSE" % tag, download_f64(lse), rl, LSE_TOL)
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 2, 1024, 1024, True), (1, 2, 1024, 1024, False),
+                                   (1, 1, 700, 700, True), (2, 3, 300, 300, False),
+                                   (1, 1, 64, 4096, False), (1, 3, 129, 2000, False)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_mfma_split_schedules(shape, dt):
+    """f16/bf16 with few query tiles: the keys are split across workgroups
+    (workspace + combine) or not (no workspace); both against the oracle, O
+    and LSE."""
+    import torch
+    B, H, Nq, Nk, causal = shape
+    q, k, v = seeded(B, H, Nq, Nk, 64, dt, 13)
+    q64, k64, v64 = (inputs.to_f64(x, dt) for x in (q, k, v))
+    ro, rl = oracle.attn(q64, k64, v64, 0.125, causal)
+    wabs = oracle.attn(q64, k64, np.abs(v64), 0.125, causal)[0]
+    tq, tk, tv = upload(q, dt), upload(k, dt), upload(v, dt)
+    code = fa2.FA2_F16 if dt == "f16" else fa2.FA2_BF16
+    need = fa2.workspace_size(B, H, Nq, Nk, 64, causal, code)
+    assert need > 0, "these shapes are meant to take the split path"
+    for use_ws in (True, False):
+        o, lse = fa2.attn_fwd(tq, tk, tv, scale=0.125, causal=causal, return_lse=True,
+                              use_workspace=use_ws)
+        torch.cuda.synchronize()
+        got = download_f64(o)
+        tag = "%s ws=%d" % (dt, use_ws)
+        assert_close("split schedule %s O" % tag, got, ro, edge_tol(dt, ro, got, wabs))
+        assert_close("split schedule %s LSE" % tag, download_f64(lse), rl, LSE_TOL)
+
+
 def test_lse_optional_and_stream_order():
     import torch
     q, k, v = seeded(1, 2, 256, 256, 64, "f16", 11)
