@@ -58,9 +58,9 @@ namespace fa2 {
 namespace {
 
 constexpr int kD = 64;
-constexpr int kBR = 128;     // query rows per workgroup
+constexpr int kBR = 128;     // query rows per workgroup with one query group per wave
 constexpr int kBC = 64;      // keys per block
-constexpr int kWaves = 4;    // 32 query rows per wave
+constexpr int kWaves = 4;    // waves per workgroup
 // A tile is accepted with the current running max when each lane's sum of its
 // 16 rounded P values is at most this (so every P <= 2^8, far below the f16
 // and bf16 overflow); otherwise the max is taken and O rescaled.
@@ -107,18 +107,23 @@ struct MfmaT<2> {
     }
 };
 
+// QG: query groups of 32 rows per wave (1 or 2).  With QG = 2 a wave owns 64
+// rows, every K and V fragment it reads from LDS feeds two MFMAs, and the
+// LDS reads per flop halve (the kernel then runs two waves per SIMD instead of
+// three).
 // SPLIT: the key blocks of each query tile are cut into gridDim.y chunks, one
 // per workgroup along y ("Flash decoding": split the keys, keep unnormalised
 // partials); the workgroup writes, per row and chunk, O_s (not divided),
 // m_s (natural-log units), the denominator of the rounded P (lt, which
 // normalises O) and, with WLSE, that of the f32 P (l, for the LSE), and the
 // combine kernel merges them.
-template <int DT, bool CAUSAL, bool WLSE, bool SPLIT>
-__global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
+template <int DT, bool CAUSAL, bool WLSE, bool SPLIT, int QG>
+__global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
     float *__restrict__ o_part, float *__restrict__ m_part, float *__restrict__ l_part,
     float *__restrict__ l2_part, int Nq, int Nk, float scale_log2, int n_qtiles, int n_tiles) {
+    constexpr int ROWS = kWaves * 32 * QG;  // query rows per workgroup
     // Two K and two V buffers of 64 rows, as separate arrays (not one indexed
     // array) so the compiler can see that reads of one never alias DMA into
     // another.  V buffer b holds keys [64b, 64b + 64) of its block; K buffer b
@@ -142,9 +147,8 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
     const int bh = wg / n_qtiles;
     int qt = wg - bh * n_qtiles;
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
-    const int q0 = qt * kBR;
-    const int qw = q0 + wave * 32;  // first row of this wave
-    const int myq = qw + ql;        // the query this lane's columns belong to
+    const int q0 = qt * ROWS;
+    const int qw = q0 + wave * 32 * QG;  // first row of this wave; group g starts at qw + 32g
 
     const uint16_t *Qh = Q + (size_t)bh * Nq * kD;
     const uint16_t *Kh = K + (size_t)bh * Nk * kD;
@@ -153,12 +157,16 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
     const auto rk = make_rsrc(Kh, (uint32_t)Nk * kD * 2);
     const auto rv = make_rsrc(Vh, (uint32_t)Nk * kD * 2);
 
-    // B operand of S^T = K Q^T: chunk dc, slot (h, j) is Q[myq][16dc + 8h + j].
-    u32x4 qf[4];
+    // B operand of S^T = K Q^T for group g: chunk dc, slot (h, j) is
+    // Q[qw + 32g + ql][16dc + 8h + j].
+    u32x4 qf[QG][4];
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) qf[dc] = load16(rq, (uint32_t)((myq * kD + 16 * dc + 8 * h) * 2));
+    for (int g = 0; g < QG; ++g)
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc)
+            qf[g][dc] = load16(rq, (uint32_t)(((qw + 32 * g + ql) * kD + 16 * dc + 8 * h) * 2));
 
-    const int kend = CAUSAL ? min(Nk, q0 + kBR) : Nk;
+    const int kend = CAUSAL ? min(Nk, q0 + ROWS) : Nk;
     const int nblk = (kend + kBC - 1) / kBC;  // 64-key V blocks of this query tile
     // This workgroup's blocks [b0, b1): all of them, or its chunk of them.
     int b0 = 0, b1 = nblk;
@@ -167,8 +175,9 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
         b0 = min(nblk, (int)blockIdx.y * nb);
         b1 = min(nblk, b0 + nb);
     }
-    // Last 32-key tile this wave needs (causal: the one holding its diagonal).
-    const int t_last = CAUSAL ? min((kend + 31) / 32 - 1, qw / 32) : 2 * nblk - 1;
+    // Last 32-key tile this wave needs (causal: the one holding the diagonal
+    // of its last row group).
+    const int t_last = CAUSAL ? min((kend + 31) / 32 - 1, (qw + 32 * (QG - 1)) / 32) : 2 * nblk - 1;
 
     // Rows past Nk are never loaded with data; make sure the V rows they
     // would occupy hold zeros (0 * V must stay 0 for the masked keys).
@@ -214,28 +223,32 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
         }
     }
 
-    float m = -INFINITY;  // max used for the exponentials, base-2 units
-    float l = 0.f;        // this lane's half of the running denominator (f32 P)
-    float lt = 0.f;       // the same over P as rounded for the MFMA
+    float m[QG], l[QG], lt[QG];  // per group: max used for the exponentials (base 2) and
+                                 // this lane's halves of the denominators (f32 P, rounded P)
     const uint32_t ones = DT == 1 ? 0x3C003C00u : 0x3F803F80u;  // (1, 1) in f16 / bf16
-    f32x16 oacc[2];
+    f32x16 oacc[QG][2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        oacc[0][i] = 0.f;
-        oacc[1][i] = 0.f;
+    for (int g = 0; g < QG; ++g) {
+        m[g] = -INFINITY;
+        l[g] = lt[g] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            oacc[g][0][i] = 0.f;
+            oacc[g][1][i] = 0.f;
+        }
     }
 
-    // One 32-key tile t.  On entry scur holds S^T of tile t (lane: query
-    // myq, register r: key 32t + 8(r/4) + 4h + r%4), kn points at the LDS
-    // rows of tile t+1's keys and vt at those of tile t's values.  With NEXT,
-    // the scores of tile t+1 go to snext; the matrix cores run them while the
-    // vector ALUs compute this tile's exponentials.
-    auto tile = [&](const int t, const uint16_t *kn, const uint16_t *vt, f32x16 &scur,
-                    f32x16 &snext, auto next_tag) {
+    // One 32-key tile t.  On entry scur[g] holds S^T of tile t for group g
+    // (lane: query qw + 32g + ql, register r: key 32t + 8(r/4) + 4h + r%4),
+    // kn points at the LDS rows of tile t+1's keys and vt at those of tile t's
+    // values.  With NEXT, the scores of tile t+1 go to snext; the matrix cores
+    // run them while the vector ALUs compute this tile's exponentials.
+    auto tile = [&](const int t, const uint16_t *kn, const uint16_t *vt, f32x16 *scur,
+                    f32x16 *snext, auto next_tag) {
         constexpr bool NEXT = decltype(next_tag)::value;
         const int k0 = 32 * t;
         // All LDS operands of this tile, issued first so their latency is
-        // covered by the max and the exponentials.
+        // covered by the exponentials.
         u32x4 kf[4];
         if constexpr (NEXT) {
 #pragma unroll
@@ -257,33 +270,36 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
         const bool need_mask = (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
         if (need_mask) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                bool ok = key < Nk;
-                if (CAUSAL) ok = ok && key <= myq;
-                if (!ok) scur[r] = -INFINITY;
-            }
+            for (int g = 0; g < QG; ++g)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    bool ok = key < Nk;
+                    if (CAUSAL) ok = ok && key <= qw + 32 * g + ql;
+                    if (!ok) scur[g][r] = -INFINITY;
+                }
         }
-        // P = exp2(S*scale*log2e - m) for this tile, rounded for the MFMA
-        // (pk), with its row sums (lp from the rounded P, ps from f32 P).
-        u32x4 pk[2];
-        float ps[2], lp[2];
-        auto exps = [&](float m_use, bool with_next) __attribute__((always_inline)) {
-            ps[0] = ps[1] = lp[0] = lp[1] = 0.f;
+        // P = exp2(S*scale*log2e - m) of group g for this tile, rounded for
+        // the MFMA (pk), with its row sums (lp from the rounded P, ps from f32 P).
+        u32x4 pk[QG][2];
+        float ps[QG][2], lp[QG][2];
+        auto exps = [&](int g, float m_use, bool with_next) __attribute__((always_inline)) {
+            ps[g][0] = ps[g][1] = lp[g][0] = lp[g][1] = 0.f;
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 8 * c + 2 * j;
-                    const float p0 = exp2f_fast(__builtin_fmaf(scur[r], scale_log2, -m_use));
-                    const float p1 = exp2f_fast(__builtin_fmaf(scur[r + 1], scale_log2, -m_use));
+                    const float p0 = exp2f_fast(__builtin_fmaf(scur[g][r], scale_log2, -m_use));
+                    const float p1 = exp2f_fast(__builtin_fmaf(scur[g][r + 1], scale_log2, -m_use));
                     const uint32_t w = pack2<DT>(p0, p1);
-                    pk[c][j] = w;
-                    if constexpr (WLSE) ps[j & 1] += p0 + p1;
-                    lp[j & 1] = dot2<DT>(w, ones, lp[j & 1]);
+                    pk[g][c][j] = w;
+                    if constexpr (WLSE) ps[g][j & 1] += p0 + p1;
+                    lp[g][j & 1] = dot2<DT>(w, ones, lp[g][j & 1]);
                     if constexpr (NEXT) {
                         // scores of the next tile, one MFMA per exponential pair of chunk 0
-                        if (with_next && c == 0) snext = MfmaT<DT>::mma(kf[j], qf[j], j == 0 ? f32x16{} : snext);
+                        if (with_next && c == 0)
+                            snext[g] = MfmaT<DT>::mma(kf[j], qf[g][j], j == 0 ? f32x16{} : snext[g]);
                     }
                 }
         };
@@ -293,9 +309,10 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
         // is, and the tile is done without computing its max.  Otherwise (and
         // on a row's first tile, where m is still -inf) take the max, rescale
         // O and the sums, and redo the exponentials.
-        exps(m == -INFINITY ? 0.f : m, true);
+#pragma unroll
+        for (int g = 0; g < QG; ++g) exps(g, m[g] == -INFINITY ? 0.f : m[g], true);
 #if FA2_SGB
-        if constexpr (NEXT) {
+        if constexpr (NEXT && QG == 1) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 __builtin_amdgcn_sched_group_barrier(0x002, WLSE ? 8 : 6, 0);
@@ -303,34 +320,43 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
             }
         }
 #endif
-        if (__builtin_amdgcn_ballot_w64(m == -INFINITY || lp[0] + lp[1] > kLazyCap) != 0) {
-            float mx = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[r]);
-            mx = max_halves(mx) * scale_log2;
-            const float m_new = fmaxf(m, mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float corr = exp2f_fast(m - m_use);
-            l *= corr;
-            lt *= corr;
+        for (int g = 0; g < QG; ++g) {
+            if (__builtin_amdgcn_ballot_w64(m[g] == -INFINITY || lp[g][0] + lp[g][1] > kLazyCap) != 0) {
+                float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                oacc[0][i] *= corr;
-                oacc[1][i] *= corr;
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[g][r]);
+                mx = max_halves(mx) * scale_log2;
+                const float m_new = fmaxf(m[g], mx);
+                const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                const float corr = exp2f_fast(m[g] - m_use);
+                l[g] *= corr;
+                lt[g] *= corr;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    oacc[g][0][i] *= corr;
+                    oacc[g][1][i] *= corr;
+                }
+                m[g] = m_new;
+                exps(g, m_use, false);
             }
-            m = m_new;
-            exps(m_use, false);
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt) oacc[dt] = MfmaT<DT>::mma(vf[c][dt], pk[c], oacc[dt]);
-        lt += lp[0] + lp[1];
-        if constexpr (WLSE) l += ps[0] + ps[1];
+            for (int g = 0; g < QG; ++g)
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt)
+                    oacc[g][dt] = MfmaT<DT>::mma(vf[c][dt], pk[g][c], oacc[g][dt]);
+#pragma unroll
+        for (int g = 0; g < QG; ++g) {
+            lt[g] += lp[g][0] + lp[g][1];
+            if constexpr (WLSE) l[g] += ps[g][0] + ps[g][1];
+        }
     };
 
-    auto run_tile = [&](const int t, const uint16_t *kn, const uint16_t *vt, f32x16 &scur,
-                        f32x16 &snext) {
+    auto run_tile = [&](const int t, const uint16_t *kn, const uint16_t *vt, f32x16 *scur,
+                        f32x16 *snext) {
         if constexpr (CAUSAL) {
             if (t > t_last) return;
             if (t + 1 <= t_last)
@@ -346,7 +372,7 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
     // K buffer kc holds keys [64b + 32, 64b + 96) (tiles 2b+1 and 2b+2);
     // block b+1 streams into vd / kd, last read in block b-1.
     auto block = [&](int b, const uint16_t *kc, uint16_t *kd, const uint16_t *vc, uint16_t *vd,
-                     f32x16 &sa, f32x16 &sb) {
+                     f32x16 *sa, f32x16 *sb) {
         if (b + 1 < b1) {
             dma(rv, vd, (b + 1) * kBC, false);
             dma(rk, kd, (b + 1) * kBC + 32, true);
@@ -368,13 +394,12 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
         dma(rk, sK1, b0 * kBC - 32, true);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        f32x16 sa, sb;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sa[i] = 0.f;
+        f32x16 sa[QG], sb[QG];
 #pragma unroll
         for (int dc = 0; dc < 4; ++dc) {
             const u32x4 a = *reinterpret_cast<const u32x4 *>(&sK1[32 * kD + kofs[dc]]);
-            sa = MfmaT<DT>::mma(a, qf[dc], sa);
+#pragma unroll
+            for (int g = 0; g < QG; ++g) sa[g] = MfmaT<DT>::mma(a, qf[g][dc], dc == 0 ? f32x16{} : sa[g]);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -386,65 +411,76 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_mfma_d64_kernel(
         }
     }
 
-    // oacc[dt][r] = O[myq][32dt + 8(r/4) + 4h + r%4] * lt
-    lt += __shfl_xor(lt, 32);
-    if constexpr (WLSE) l += __shfl_xor(l, 32);
+    // oacc[g][dt][r] = O[qw + 32g + ql][32dt + 8(r/4) + 4h + r%4] * lt[g]
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+        lt[g] += __shfl_xor(lt[g], 32);
+        if constexpr (WLSE) l[g] += __shfl_xor(l[g], 32);
+    }
     if constexpr (SPLIT) {
-        // Partials: stage this wave's 32 rows x 64 columns in LDS (each wave
-        // its own 8 KB buffer, free after the last barrier) so that each row's
-        // 256 bytes go out as one contiguous piece.
+        // Partials: stage 32 rows x 64 columns at a time in LDS (each wave its
+        // own 8 KB buffer, free after the last barrier) so that each row's 256
+        // bytes go out as one contiguous piece.
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         float *stage = reinterpret_cast<float *>(wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1);
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int r = 4 * g4;
-                *reinterpret_cast<f32x4 *>(stage + ql * kD + ((32 * dt + 8 * g4 + 4 * h) ^ (4 * (ql & 7)))) =
-                    f32x4{oacc[dt][r], oacc[dt][r + 1], oacc[dt][r + 2], oacc[dt][r + 3]};
-            }
         const size_t nch = gridDim.y;
-        if (myq < Nq && h == 0) {
-            const size_t pidx = ((size_t)bh * Nq + myq) * nch + blockIdx.y;
-            m_part[pidx] = m == -INFINITY ? -INFINITY : m * kLn2;  // natural-log units
-            l_part[pidx] = lt;
-            if constexpr (WLSE) l2_part[pidx] = l;
-        }
-        // lane i of each 16-lane group writes 16 bytes of row 4j + lane/16
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = 4 * j + (lane >> 4);
-            const int col = 4 * (lane & 15);
-            const int q = qw + row;
-            const f32x4 val = *reinterpret_cast<const f32x4 *>(stage + row * kD + (col ^ (4 * (row & 7))));
-            if (q < Nq)
-                *reinterpret_cast<f32x4 *>(o_part + (((size_t)bh * Nq + q) * nch + blockIdx.y) * kD + col) = val;
+        for (int g = 0; g < QG; ++g) {
+            const int myq = qw + 32 * g + ql;
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int r = 4 * g4;
+                    *reinterpret_cast<f32x4 *>(stage + ql * kD + ((32 * dt + 8 * g4 + 4 * h) ^ (4 * (ql & 7)))) =
+                        f32x4{oacc[g][dt][r], oacc[g][dt][r + 1], oacc[g][dt][r + 2], oacc[g][dt][r + 3]};
+                }
+            if (myq < Nq && h == 0) {
+                const size_t pidx = ((size_t)bh * Nq + myq) * nch + blockIdx.y;
+                m_part[pidx] = m[g] == -INFINITY ? -INFINITY : m[g] * kLn2;  // natural-log units
+                l_part[pidx] = lt[g];
+                if constexpr (WLSE) l2_part[pidx] = l[g];
+            }
+            // lane i of each 16-lane group writes 16 bytes of row 4j + lane/16
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int row = 4 * j + (lane >> 4);
+                const int col = 4 * (lane & 15);
+                const int q = qw + 32 * g + row;
+                const f32x4 val = *reinterpret_cast<const f32x4 *>(stage + row * kD + (col ^ (4 * (row & 7))));
+                if (q < Nq)
+                    *reinterpret_cast<f32x4 *>(o_part + (((size_t)bh * Nq + q) * nch + blockIdx.y) * kD + col) = val;
+            }
         }
         return;
     }
-    if (myq < Nq) {
-        const float inv = 1.f / lt;
-        uint16_t *orow = O + ((size_t)bh * Nq + myq) * kD;
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+    for (int g = 0; g < QG; ++g) {
+        const int myq = qw + 32 * g + ql;
+        if (myq < Nq) {
+            const float inv = 1.f / lt[g];
+            uint16_t *orow = O + ((size_t)bh * Nq + myq) * kD;
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int d = 32 * dt + 8 * g4 + 4 * h;
-                const int r = 4 * g4;
-                u32x2 w;
-                w[0] = pack2<DT>(oacc[dt][r] * inv, oacc[dt][r + 1] * inv);
-                w[1] = pack2<DT>(oacc[dt][r + 2] * inv, oacc[dt][r + 3] * inv);
-                *reinterpret_cast<u32x2 *>(orow + d) = w;
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d = 32 * dt + 8 * g4 + 4 * h;
+                    const int r = 4 * g4;
+                    u32x2 w;
+                    w[0] = pack2<DT>(oacc[g][dt][r] * inv, oacc[g][dt][r + 1] * inv);
+                    w[1] = pack2<DT>(oacc[g][dt][r + 2] * inv, oacc[g][dt][r + 3] * inv);
+                    *reinterpret_cast<u32x2 *>(orow + d) = w;
+                }
+            if constexpr (WLSE) {
+                if (h == 0) LSE[(size_t)bh * Nq + myq] = (m[g] + log2f_fast(l[g])) * kLn2;
             }
-        if constexpr (WLSE) {
-            if (h == 0) LSE[(size_t)bh * Nq + myq] = (m + log2f_fast(l)) * kLn2;
         }
     }
 }
 
 struct Plan {
-    int n_qtiles, n_tiles, chunks;
+    int qg, n_qtiles, n_tiles, chunks;
 };
 
 #ifndef FA2_MFMA_SPLIT_WGS
@@ -453,13 +489,23 @@ struct Plan {
 #ifndef FA2_MFMA_SPLIT_BELOW
 #define FA2_MFMA_SPLIT_BELOW 8  // split only with at most num_cus / this many query tiles
 #endif
+#ifndef FA2_MFMA_QG2
+#define FA2_MFMA_QG2 1  // 1: 64 query rows per wave when the tiles fill the device twice over; 2: always
+#endif
 
-// Split the keys of each query tile when the query tiles fill at most an
-// eighth of the compute units (with more, writing and merging the partials
-// costs more than the idle units), into at most one chunk per two key blocks.
+// Query groups per wave: 64-row waves when the 256-row tiles make whole
+// rounds of two per compute unit.  Keys: split the keys of each query tile
+// when the query tiles fill at most an eighth of the compute units (with
+// more, writing and merging the partials costs more than the idle units),
+// into at most one chunk per two key blocks.
 Plan plan(int B, int H, int Nq, int Nk, int num_cus) {
     Plan p;
-    p.n_qtiles = (Nq + kBR - 1) / kBR;
+    p.qg = 1;
+    if (FA2_MFMA_QG2) {
+        const long long nt2 = (long long)((Nq + 2 * kBR - 1) / (2 * kBR)) * B * H;
+        if (FA2_MFMA_QG2 == 2 || (nt2 >= 2LL * num_cus && nt2 % (2LL * num_cus) == 0)) p.qg = 2;
+    }
+    p.n_qtiles = (Nq + kBR * p.qg - 1) / (kBR * p.qg);
     const long long nt = (long long)p.n_qtiles * B * H;
     p.n_tiles = nt > 0x7FFFFFFF ? -1 : (int)nt;
     p.chunks = 1;
@@ -476,8 +522,8 @@ size_t part_bytes(const FwdArgs &a, int chunks) {
     return (size_t)a.B * a.H * a.Nq * chunks * (kD + 3) * sizeof(float);
 }
 
-template <int DT, bool CAUSAL, bool WLSE>
-fa2_status launch_v(const FwdArgs &a, const Plan &p, hipStream_t st) {
+template <int DT, bool CAUSAL, bool WLSE, int QG>
+fa2_status launch_q(const FwdArgs &a, const Plan &p, hipStream_t st) {
     const uint16_t *q = (const uint16_t *)a.q, *k = (const uint16_t *)a.k, *v = (const uint16_t *)a.v;
     const float sl2 = a.scale * kLog2e;
     if (p.chunks > 1 && a.ws && a.ws_bytes >= part_bytes(a, p.chunks)) {
@@ -486,7 +532,7 @@ fa2_status launch_v(const FwdArgs &a, const Plan &p, hipStream_t st) {
         float *m_part = o_part + n * kD;
         float *l_part = m_part + n;
         float *l2_part = l_part + n;
-        fa2_status s = launch(fwd_mfma_d64_kernel<DT, CAUSAL, WLSE, true>,
+        fa2_status s = launch(fwd_mfma_d64_kernel<DT, CAUSAL, WLSE, true, QG>,
                               dim3((unsigned)p.n_tiles, (unsigned)p.chunks), dim3(kWaves * 64), st,
                               q, k, v, (uint16_t *)a.o, a.lse, o_part, m_part, l_part, l2_part, a.Nq,
                               a.Nk, sl2, p.n_qtiles, p.n_tiles);
@@ -495,10 +541,18 @@ fa2_status launch_v(const FwdArgs &a, const Plan &p, hipStream_t st) {
                                    p.chunks, DT == 1 ? FA2_F16 : FA2_BF16, st,
                                    WLSE ? l2_part : nullptr);
     }
-    return launch(fwd_mfma_d64_kernel<DT, CAUSAL, WLSE, false>, dim3((unsigned)p.n_tiles),
+    return launch(fwd_mfma_d64_kernel<DT, CAUSAL, WLSE, false, QG>, dim3((unsigned)p.n_tiles),
                   dim3(kWaves * 64), st, q, k, v, (uint16_t *)a.o, a.lse, (float *)nullptr,
                   (float *)nullptr, (float *)nullptr, (float *)nullptr, a.Nq, a.Nk, sl2,
                   p.n_qtiles, p.n_tiles);
+}
+
+template <int DT, bool CAUSAL, bool WLSE>
+fa2_status launch_v(const FwdArgs &a, const Plan &p, hipStream_t st) {
+    if constexpr (FA2_MFMA_QG2 != 0) {
+        if (p.qg == 2) return launch_q<DT, CAUSAL, WLSE, 2>(a, p, st);
+    }
+    return launch_q<DT, CAUSAL, WLSE, 1>(a, p, st);
 }
 
 template <int DT>

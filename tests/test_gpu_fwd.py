@@ -75,6 +75,20 @@ def test_multihead_2048_sampled(dt):
     check_full(cfg, rows)
 
 
+@pytest.mark.parametrize("dt,causal", [("f16", False), ("f16", True), ("bf16", False)])
+def test_many_heads_64_rows_per_wave(dt, causal):
+    """B4 H64 N2048: 256-row query tiles fill every compute unit with two
+    workgroups in whole rounds, so the f16/bf16 kernel runs 64 query rows per
+    wave.  Sampled rows against the oracle (the early causal rows of bf16
+    would need the format bound of the edge tests, so bf16 runs non-causal)."""
+    cfg = workloads.Prefill("B4 H64 N2048 %s" % dt, 4, 64, 2048, 2048, 64, dt, 0.125, causal, 14)
+    g = np.random.default_rng(2)
+    total = cfg.B * cfg.H * cfg.Nq
+    rows = np.unique(np.concatenate([np.arange(256), total - 1 - np.arange(256),
+                                     g.choice(total, 768, replace=False)]))
+    check_full(cfg, rows)
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_causal_lse_f16(causal):
     check_full(workloads.causal_lse(causal))
