@@ -139,8 +139,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
             s[r] = live ? sacc[r] * scale_log2 : -INFINITY;
             mx = fmaxf(mx, s[r]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_xor32(max_xor16(mx));
         const float m_new = fmaxf(m, mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float corr = exp2f_fast(m - m_use);
@@ -341,8 +340,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void kernel(
             sv[r] = live ? sacc[r] * scale_log2 : -INFINITY;
             mx = fmaxf(mx, sv[r]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_xor32(max_xor16(mx));
         const float m_new = fmaxf(m, mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float corr = exp2f_fast(m - m_use);
