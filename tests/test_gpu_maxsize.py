@@ -1,0 +1,81 @@
+"""The largest (b,h) slices the library accepts: just under 2 GiB of K and of
+V per (batch, head), where 32-bit offset arithmetic would first go wrong.
+
+No host oracle at this size; the inputs are built so the answer is exact:
+* K = 0 makes every score 0, so every key weighs the same; with V = +1 for the
+  first half of the keys and -1 for the second half, O = 0 exactly (all sums
+  are small integers in float32) and LSE = ln(Nk).
+* One key k_j = 16 q (a spike) outscores the rest by more than 150 in natural
+  units, so O = V_j to within e^-150 relative; j near either end of the slice
+  checks that the last and first rows are addressed.
+"""
+import math
+
+import pytest
+
+from exact_attention_fa2_amd import fa2
+
+pytestmark = pytest.mark.gpu
+
+MAX_SLICE = (1 << 31) - (1 << 20)  # bytes of K (or V) per (b,h) the library accepts
+
+
+def _kv(n, d, dtype):
+    import torch
+    k = torch.zeros((1, 1, n, d), dtype=dtype, device="cuda")
+    v = torch.ones((1, 1, n, d), dtype=dtype, device="cuda")
+    v[:, :, n // 2:] = -1
+    return k, v
+
+
+def _free(*ts):
+    import torch
+    del ts
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_decode_largest_slice(dt):
+    import torch
+    dtype = torch.float16 if dt == "f16" else torch.bfloat16
+    D = 128
+    N = MAX_SLICE // (D * 2)
+    k, v = _kv(N, D, dtype)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    q = torch.randn((1, 1, D), generator=g, device="cuda").to(dtype)
+    o = fa2.attn_decode(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o).item() == 0, o.abs().max().item()
+    for j, want in ((N - 3, -1.0), (2, 1.0)):
+        k[0, 0, j] = (16 * q[0, 0].float()).to(dtype)
+        o = fa2.attn_decode(q, k, v).float()
+        torch.cuda.synchronize()
+        assert (o - want).abs().max().item() <= 4e-3, (j, o[0, 0, :4])
+        k[0, 0, j] = 0
+    _free(k, v, q, o)
+
+
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+def test_forward_largest_slice(dt):
+    import torch
+    dtype = torch.float16 if dt == "f16" else torch.float32
+    es = 2 if dt == "f16" else 4
+    D = 64
+    Nk = MAX_SLICE // (D * es)
+    Nq = 100  # one ragged query tile: the keys are split across workgroups
+    k, v = _kv(Nk, D, dtype)
+    g = torch.Generator(device="cuda").manual_seed(6)
+    qrow = torch.randn((1, 1, 1, D), generator=g, device="cuda").to(dtype)
+    q = qrow.expand(1, 1, Nq, D).contiguous()
+    o, lse = fa2.attn_fwd(q, k, v, scale=0.125, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o).item() == 0, o.abs().max().item()
+    assert (lse - math.log(Nk)).abs().max().item() <= 1e-4
+    for j, want in ((Nk - 3, -1.0), (2, 1.0)):
+        k[0, 0, j] = (16 * qrow[0, 0, 0].float()).to(dtype)
+        o = fa2.attn_fwd(q, k, v, scale=0.125).float()
+        torch.cuda.synchronize()
+        assert (o - want).abs().max().item() <= 4e-3, (j, o[0, 0, 0, :4])
+        k[0, 0, j] = 0
+    _free(k, v, q, o, lse)
