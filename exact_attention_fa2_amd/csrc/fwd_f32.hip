@@ -449,12 +449,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void kernel(
 // Split only when even 16-row workgroups cannot cover the device: with one
 // 16-row workgroup per compute unit or more, the unsplit kernels measured
 // faster than split + combine.
+#ifndef FA2_F32_SPLIT_BELOW
+#define FA2_F32_SPLIT_BELOW 1  // split while 16-row tiles < this many per compute unit
+#endif
+#ifndef FA2_F32_SPLIT_WAVES
+#define FA2_F32_SPLIT_WAVES 1  // chunks so that groups x chunks = this many per compute unit
+#endif
+
 int f32_chunks(int B, int H, int Nq, int Nk, int num_cus) {
     const long long groups = (long long)B * H * ((Nq + shared::kRows - 1) / shared::kRows);
     const long long tiles16 = (long long)B * H * ((Nq + kQT - 1) / kQT);
-    if (groups >= num_cus || tiles16 >= num_cus) return 1;
+    if (groups >= num_cus || tiles16 >= (long long)FA2_F32_SPLIT_BELOW * num_cus) return 1;
     const int nsteps = (Nk + kStep - 1) / kStep;
-    long long c = (num_cus + groups - 1) / groups;
+    long long c = ((long long)FA2_F32_SPLIT_WAVES * num_cus + groups - 1) / groups;
     c = std::min<long long>(c, std::max(1, nsteps / shared::kSub));  // >= one step per sub-slice
     c = std::min<long long>(c, 64);
     return (int)std::max<long long>(1, c);
