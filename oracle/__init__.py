@@ -15,6 +15,10 @@ Contents
   * ``decode_split`` / ``decode_combine`` -- flash-decoding partials and their
     merge, "Flash decoding", Overview of the algorithm (split and combine
     equations), with the scale inside the score as the page's split kernel has it.
+  * ``attn_bwd`` -- the gradients dQ, dK, dV of O = softmax(scale Q K^T) V for an
+    upstream dO, and D = rowsum(dO o O), from the plain chain rule in fp64
+    ("Flash Attention", section IO complexity, the backward pass: D_i and
+    dS = P o (dP - D_i); "06: Fused attention", the backward kernels).
   * ``brute`` -- a pure-Python brute force for tiny inputs (no max subtraction).
   * ``recurrence`` -- the tiled online-softmax recurrence in fp64, used only to
     show that the recurrence equals the batched definition.
@@ -25,6 +29,9 @@ invariance with shifts far past exp's f32 overflow, key-permutation invariance,
 convex-hull bounds, the tiled recurrence for many block sizes, the (m, l) monoid
 under random groupings, split-then-combine = unsplit, hand-derived golden cases
 in tests/golden/, and torch's CPU float64 attention as a library cross-check.
+Backward: central finite differences of the forward definition, closed forms
+(constant V rows give dQ = dK = 0; K = 0 gives dV = column means of dO), and
+torch's CPU float64 autograd.
 """
 from __future__ import annotations
 
@@ -71,6 +78,10 @@ class Oracle:
         lib.oracle_decode_combine.argtypes = [dp, dp, dp, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, ctypes.c_int, dp]
         lib.oracle_decode_combine.restype = ctypes.c_int
+        lib.oracle_attn_bwd.argtypes = [dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                        llp, ctypes.c_longlong, dp, dp, dp, dp, ctypes.c_int]
+        lib.oracle_attn_bwd.restype = ctypes.c_int
         self.lib = lib
 
 
@@ -176,3 +187,35 @@ def decode_combine(o_part, m_part, l_part, lib=None):
     if rc != 0:
         raise ValueError("oracle_decode_combine rejected its arguments")
     return o
+
+
+def attn_bwd(q, k, v, dout, scale: float, causal: bool = False, heads=None, nthreads: int = 0,
+             lib=None):
+    """Gradients of O = softmax(scale Q K^T) V (masked keys left out).
+
+    q, dout [B,H,Nq,D], k/v [B,H,Nk,D] float64.  ``heads`` holds flat head ids
+    b*H + h (``None`` = every head).  Returns (dq [n,Nq,D], dk [n,Nk,D],
+    dv [n,Nk,D], delta [n,Nq]) for the n selected heads.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, D) or v.shape != (B, H, Nk, D) or dout.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if heads is None:
+        n = B * H
+        hp = None
+    else:
+        heads = np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+        n = heads.size
+        hp = _ptr(heads, ctypes.c_longlong)
+    dq = np.empty((n, Nq, D), dtype=np.float64)
+    dk = np.empty((n, Nk, D), dtype=np.float64)
+    dv = np.empty((n, Nk, D), dtype=np.float64)
+    delta = np.empty((n, Nq), dtype=np.float64)
+    rc = (lib or _load()).oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, Nq, Nk, D,
+                                          float(scale), int(bool(causal)), hp, n, _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _ptr(delta), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attn_bwd rejected its arguments")
+    return dq, dk, dv, delta

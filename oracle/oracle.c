@@ -27,10 +27,19 @@
  *       Scores include the scale factor (the page's split kernel multiplies
  *       the dot product by `scale`; its equations omit it).  Split size is
  *       S = ceil(N / n_splits); a split with no keys holds (-inf, 0, 0).
+ *   Backward pass ("Flash Attention", section IO complexity, the paragraph on
+ *       the backward pass; "06: Fused attention", the backward kernels): with
+ *       P = softmax(scale Q K^T) (masked keys left out) and the upstream
+ *       gradient dO of O = P V,
+ *         dV = P^T dO,   dP = dO V^T,   D_i = rowsum(dO o O)_i,
+ *         dS = P o (dP - D_i),   dQ = scale dS K,   dK = scale dS^T Q.
+ *       D_i equals sum_j P_ij dP_ij, the term the softmax Jacobian reduces to.
  *
  * Layouts (all contiguous row-major, fp64):
  *   q [B,H,Nq,D], k and v [B,H,Nk,D], o [rows,D], lse [rows].
  *   A "row id" is r = (b*H + h)*Nq + i.
+ *   Backward: dout [B,H,Nq,D]; for each selected head t: dq [t][Nq][D],
+ *   dk and dv [t][Nk][D], delta [t][Nq].
  *
  * Return value: 0 on success, -1 on an invalid argument.
  */
@@ -182,4 +191,109 @@ int oracle_decode_combine(const double *o_part, const double *m_part,
         }
     }
     return 0;
+}
+
+/* Gradients of O = softmax(scale Q K^T) V for the heads listed in `heads`
+ * (indices b*H + h; every head when heads == NULL).  Per head the whole
+ * probability matrix is formed in fp64 (Nq x Nk doubles of scratch). */
+int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
+                    int B, int H, int Nq, int Nk, int D, double scale, int causal,
+                    const long long *heads, long long nheads,
+                    double *dq, double *dk, double *dv, double *delta, int nthreads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || !delta) return -1;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1) return -1;
+    if (causal && Nq != Nk) return -1;
+    const long long total = (long long)B * H;
+    if (!heads) nheads = total;
+    if (nheads < 0) return -1;
+    for (long long t = 0; t < nheads && heads; ++t)
+        if (heads[t] < 0 || heads[t] >= total) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *P = (double *)malloc(sizeof(double) * (size_t)Nq * Nk);
+        double *O = (double *)malloc(sizeof(double) * (size_t)Nq * D);
+        if (!P || !O) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long long t = 0; t < nheads; ++t) {
+            if (!P || !O) continue;
+            const long long bh = heads ? heads[t] : t;
+            const double *qh = q + (size_t)bh * Nq * D;
+            const double *kh = k + (size_t)bh * Nk * D;
+            const double *vh = v + (size_t)bh * Nk * D;
+            const double *gh = dout + (size_t)bh * Nq * D;
+            double *dqh = dq + (size_t)t * Nq * D;
+            double *dkh = dk + (size_t)t * Nk * D;
+            double *dvh = dv + (size_t)t * Nk * D;
+            double *dlt = delta + (size_t)t * Nq;
+            /* P: the softmax of each row over its live keys, 0 for masked keys */
+            for (int i = 0; i < Nq; ++i) {
+                const int nlive = causal ? i + 1 : Nk;
+                double *pr = P + (size_t)i * Nk;
+                double mx = -INFINITY;
+                for (int j = 0; j < nlive; ++j) {
+                    double acc = 0.0;
+                    for (int d = 0; d < D; ++d) acc += qh[(size_t)i * D + d] * kh[(size_t)j * D + d];
+                    pr[j] = scale * acc;
+                    if (pr[j] > mx) mx = pr[j];
+                }
+                double z = 0.0;
+                for (int j = 0; j < nlive; ++j) {
+                    pr[j] = exp(pr[j] - mx);
+                    z += pr[j];
+                }
+                for (int j = 0; j < nlive; ++j) pr[j] /= z;
+                for (int j = nlive; j < Nk; ++j) pr[j] = 0.0;
+            }
+            /* O = P V and D_i = rowsum(dO o O) */
+            for (int i = 0; i < Nq; ++i) {
+                double di = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    double acc = 0.0;
+                    for (int j = 0; j < Nk; ++j) acc += P[(size_t)i * Nk + j] * vh[(size_t)j * D + d];
+                    O[(size_t)i * D + d] = acc;
+                    di += gh[(size_t)i * D + d] * acc;
+                }
+                dlt[i] = di;
+            }
+            /* dV = P^T dO */
+            for (int j = 0; j < Nk; ++j)
+                for (int d = 0; d < D; ++d) {
+                    double acc = 0.0;
+                    for (int i = 0; i < Nq; ++i) acc += P[(size_t)i * Nk + j] * gh[(size_t)i * D + d];
+                    dvh[(size_t)j * D + d] = acc;
+                }
+            /* dS = P o (dO V^T - D_i), stored over P */
+            for (int i = 0; i < Nq; ++i)
+                for (int j = 0; j < Nk; ++j) {
+                    double dp = 0.0;
+                    for (int d = 0; d < D; ++d) dp += gh[(size_t)i * D + d] * vh[(size_t)j * D + d];
+                    P[(size_t)i * Nk + j] *= dp - dlt[i];
+                }
+            /* dQ = scale dS K,  dK = scale dS^T Q */
+            for (int i = 0; i < Nq; ++i)
+                for (int d = 0; d < D; ++d) {
+                    double acc = 0.0;
+                    for (int j = 0; j < Nk; ++j) acc += P[(size_t)i * Nk + j] * kh[(size_t)j * D + d];
+                    dqh[(size_t)i * D + d] = scale * acc;
+                }
+            for (int j = 0; j < Nk; ++j)
+                for (int d = 0; d < D; ++d) {
+                    double acc = 0.0;
+                    for (int i = 0; i < Nq; ++i) acc += P[(size_t)i * Nk + j] * qh[(size_t)i * D + d];
+                    dkh[(size_t)j * D + d] = scale * acc;
+                }
+        }
+        free(P);
+        free(O);
+    }
+    return bad ? -1 : 0;
 }
