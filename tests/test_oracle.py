@@ -293,9 +293,10 @@ MUTANTS = [
     ("wrong max sign", "s[j] = exp(s[j] - mx);", "s[j] = exp(s[j] + mx);"),
     ("missing normalisation", "for (int d = 0; d < D; ++d) orow[d] /= z;", ""),
     ("LSE without max", "if (lse) *lse = mx + log(z);", "if (lse) *lse = log(z);"),
-    ("causal off by one", "const int nlive = causal ? i + 1 : Nk;",
-     "const int nlive = causal ? i : Nk;"),
-    ("causal ignored", "const int nlive = causal ? i + 1 : Nk;", "const int nlive = Nk;"),
+    ("causal off by one", "const int nlive = causal ? i + 1 : Nk;\n            one_row(",
+     "const int nlive = causal ? i : Nk;\n            one_row("),
+    ("causal ignored", "const int nlive = causal ? i + 1 : Nk;\n            one_row(",
+     "const int nlive = Nk;\n            one_row("),
     ("V row index", "const double *vr = vh + (size_t)j * D;",
      "const double *vr = vh + (size_t)(Nk - 1 - j) * D;"),
     ("split size floor", "const long long S = ((long long)N + n_splits - 1) / n_splits;",
