@@ -100,6 +100,30 @@ FA2_API size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int 
     return fa2::mfma_workspace_bytes(B, H, Nq, Nk, causal, cus);
 }
 
+FA2_API fa2_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                            const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                            float *delta, int B, int H, int Nq, int Nk, int D, float scale,
+                            int causal, fa2_dtype dtype, void *stream) {
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 1 || D < 1) return FA2_ERR_SHAPE;
+    if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return FA2_ERR_UNSUPPORTED;
+    if (D != 64 || dtype == FA2_F32) return FA2_ERR_UNSUPPORTED;
+    if (causal && Nq != Nk) return FA2_ERR_UNSUPPORTED;
+    if ((long long)B * H == 0) return FA2_OK;
+    if (!k || !v || !dk || !dv) return FA2_ERR_NULL;
+    if (Nq > 0 && (!q || !o || !dout || !lse || !dq || !delta)) return FA2_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(lse) || !aligned16(delta))
+        return FA2_ERR_ALIGN;
+    const long long es = esize(dtype);
+    if ((long long)Nk * D * es > kMaxSliceBytes || (long long)Nq * D * es > kMaxSliceBytes)
+        return FA2_ERR_UNSUPPORTED;
+    if ((long long)B * H > 65535) return FA2_ERR_UNSUPPORTED;
+    if (!current_device()) return FA2_ERR_DEVICE;
+    fa2::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, scale, causal};
+    return fa2::launch_bwd_mfma_d64(a, dtype, (hipStream_t)stream);
+}
+
 FA2_API fa2_status attn_decode_split(const void *q, const void *k, const void *v,
                                      float *o_part, float *m_part, float *l_part, int B, int H,
                                      int N, int D, float scale, int n_splits, fa2_dtype dtype,

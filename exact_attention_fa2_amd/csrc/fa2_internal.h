@@ -32,6 +32,18 @@ size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int num_cus);
 fa2_status launch_fwd_mfma_d64(const FwdArgs &a, fa2_dtype dt, hipStream_t st);
 size_t mfma_workspace_bytes(int B, int H, int Nq, int Nk, int causal, int num_cus);
 
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    void *dq, *dk, *dv;
+    float *delta;
+    int B, H, Nq, Nk;
+    float scale;
+    int causal;
+};
+
+fa2_status launch_bwd_mfma_d64(const BwdArgs &a, fa2_dtype dt, hipStream_t st);
+
 struct DecodeArgs {
     const void *q, *k, *v;
     float *o_part, *m_part, *l_part;

@@ -18,7 +18,7 @@ STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "unsupported config
           4: "pointer not 16-byte aligned", 5: "kernel launch failed",
           6: "no usable gfx950 device"}
 
-EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "attn_decode_split",
+EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "attn_bwd", "attn_decode_split",
            "attn_decode_combine", "attn_decode_default_splits", "fa2_status_string")
 
 _lib = None
@@ -45,6 +45,8 @@ def lib():
         L.attn_fwd_ws.restype = i
         L.attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
         L.attn_fwd_workspace_size.restype = ctypes.c_size_t
+        L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, fp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp]
+        L.attn_bwd.restype = i
         L.attn_decode_split.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, f, i, i, vp]
         L.attn_decode_split.restype = i
         L.attn_decode_combine.argtypes = [fp, fp, fp, vp, i, i, i, i, i, vp]
@@ -135,6 +137,38 @@ def attn_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=
                            _stream(stream))
     _check("attn_fwd", st)
     return (out, lse) if return_lse else out
+
+
+def attn_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None,
+             delta=None, stream=None):
+    """Exact attention backward.  q/o/dout [B,H,Nq,D], k/v [B,H,Nk,D] (same
+    dtype), lse [B,H,Nq] float32 from attn_fwd.  Returns (dq, dk, dv, delta)
+    with delta [B,H,Nq] float32 = rowsum(dout * o)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)):
+        _contig(t, name)
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, D) or v.shape != (B, H, Nk, D):
+        raise ValueError("k and v must be [B,H,Nk,D] matching q")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B,H,Nq]")
+    if any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise TypeError("q, k, v, o and dout must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                        _ptr(dk), _ptr(dv), _ptr(delta), B, H, Nq, Nk, D, float(scale),
+                        int(bool(causal)), dtype_code(q), _stream(stream))
+    _check("attn_bwd", st)
+    return dq, dk, dv, delta
 
 
 def attn_decode_split(q, k, v, scale, n_splits, o_part=None, m_part=None, l_part=None,

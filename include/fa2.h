@@ -109,6 +109,41 @@ fa2_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, flo
 size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int causal, fa2_dtype dtype);
 
 /*
+ * attn_bwd -- exact attention backward: gradients of attn_fwd's o with
+ * respect to q, k and v, given the upstream gradient dout.
+ *
+ * With P_ij = exp(s_ij - lse_i) the probabilities of the forward (s_ij as in
+ * attn_fwd, 0 for keys that are not live) and
+ *     delta[b,h,i] = sum_d dout[b,h,i,d] o[b,h,i,d]
+ *     dS_ij = P_ij (dout_i . v_j - delta_i)
+ *     dv_j = sum_i P_ij dout_i,  dq_i = scale sum_j dS_ij k_j,
+ *     dk_j = scale sum_i dS_ij q_i
+ * ("Flash Attention" (aarnphm.xyz): section IO complexity, the backward
+ * pass -- only O and the log-sum-exp are kept, P is recomputed block by
+ * block; "06: Fused attention": the backward kernels, the pre-pass for
+ * delta, the dK/dV pass over query blocks and the dQ pass over key blocks).
+ * No Nq x Nk matrix is stored.
+ *
+ *   q, o, dout  [B,H,Nq,D] dtype      k, v [B,H,Nk,D] dtype
+ *   lse         [B,H,Nq] float32, natural log, as written by attn_fwd for
+ *               the same q, k, scale and causal flag
+ *   dq [B,H,Nq,D], dk, dv [B,H,Nk,D] dtype: outputs, rounded to nearest-even
+ *   delta       [B,H,Nq] float32: output (the library fills it and then
+ *               reads it; its contents on entry are ignored)
+ *   causal, scale  as in attn_fwd (causal requires Nq == Nk)
+ *   Arithmetic: the four products per block run on MFMA with float32
+ *   accumulation; P and dS are rounded to dtype before the two products
+ *   that consume them (as P is in attn_fwd); delta, P and dS are formed in
+ *   float32.  With Nq == 0, dk and dv are set to zero.
+ *   Supported: D == 64; dtype F16, BF16 (F32 -> FA2_ERR_UNSUPPORTED); any
+ *   B, H, Nq >= 0 (B*H == 0 enqueues nothing); Nk >= 1.
+ */
+fa2_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                    const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                    float *delta, int B, int H, int Nq, int Nk, int D, float scale,
+                    int causal, fa2_dtype dtype, void *stream);
+
+/*
  * attn_decode_split -- flash-decoding, phase 1: unnormalised partials.
  *
  * One query row per (b,h) attends all N keys of its slice, with the keys cut

@@ -128,3 +128,35 @@ def test_workspace_size_plan():
     # float32: one head of 4096 rows is split, many heads are not
     assert fa2.workspace_size(1, 1, 4096, 4096, 64, 0, f32) >= 0
     assert fa2.workspace_size(8, 48, 256, 256, 64, 0, f32) == 0
+
+
+def _bwd(q=1, k=1, v=1, o=1, g=1, lse=1, dq=1, dk=1, dv=1, delta=1, B=1, H=1, Nq=4, Nk=4, D=64,
+         causal=0, dt=fa2.FA2_F16):
+    p = lambda x: None if x is None else ctypes.c_void_p(x * 4096)  # noqa: E731
+    return fa2.lib().attn_bwd(p(q), p(k), p(v), p(o), p(g), p(lse), p(dq), p(dk), p(dv), p(delta),
+                              B, H, Nq, Nk, D, 0.125, causal, dt, None)
+
+
+def test_bwd_error_paths():
+    assert _bwd(Nk=0) == 2
+    assert _bwd(Nq=-1) == 2
+    assert _bwd(D=0) == 2
+    assert _bwd(D=128) == 3
+    assert _bwd(dt=fa2.FA2_F32) == 3
+    assert _bwd(dt=9) == 3
+    assert _bwd(causal=1, Nq=4, Nk=8) == 3
+    assert _bwd(causal=3) == 3
+    for name in ("q", "k", "v", "o", "g", "lse", "dq", "dk", "dv", "delta"):
+        assert _bwd(**{name: None}) == 1, name
+    # with no queries only k, v, dk and dv are needed
+    assert _bwd(q=None, o=None, g=None, lse=None, dq=None, delta=None, Nq=0, dk=None) == 1
+    ok, mis = ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 4)
+    L = fa2.lib()
+    for pos in range(10):
+        ptrs = [ok] * 10
+        ptrs[pos] = mis
+        assert L.attn_bwd(*ptrs, 1, 1, 4, 4, 64, 0.1, 0, 1, None) == 4, pos
+    assert _bwd(Nk=1 << 24) == 3
+    assert _bwd(B=300, H=300) == 3
+    # B*H == 0: a valid no-op, even with NULL pointers
+    assert fa2.lib().attn_bwd(*([None] * 10), 0, 4, 4, 4, 64, 0.1, 0, 1, None) == 0
