@@ -119,6 +119,8 @@ FA2_API fa2_status attn_bwd(const void *q, const void *k, const void *v, const v
     if ((long long)Nk * D * es > kMaxSliceBytes || (long long)Nq * D * es > kMaxSliceBytes)
         return FA2_ERR_UNSUPPORTED;
     if ((long long)B * H > 65535) return FA2_ERR_UNSUPPORTED;
+    // one workgroup per 128 rows of each (b,h): the grid holds fewer than 2^24
+    if ((long long)((Nq > Nk ? Nq : Nk) + 127) / 128 * B * H >= (1LL << 24)) return FA2_ERR_UNSUPPORTED;
     if (!current_device()) return FA2_ERR_DEVICE;
     fa2::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, scale, causal};
     return fa2::launch_bwd_mfma_d64(a, dtype, (hipStream_t)stream);

@@ -21,10 +21,26 @@
 //   dK/dV:      S = Q K^T and dP = dO V^T (queries x keys, one key per lane),
 //               dV^T += dO^T P and dK^T += Q^T dS, dO^T and Q^T transposed
 //               from LDS.
-// Every LDS tile that is read both by rows (b128) and transposed (tr_b16)
-// swizzles its 16-byte chunks by row % 8.
+// Every LDS tile is read both by rows (b128) and transposed (tr_b16); its
+// 16-byte chunks are swizzled so that neither read has bank conflicts.
+#include <type_traits>
+
 #include "fa2_device.h"
 #include "fa2_internal.h"
+
+// Waves per SIMD the dK/dV kernel is compiled for (its register budget).
+#ifndef FA2_BWD_KV_OCC
+#define FA2_BWD_KV_OCC 2
+#endif
+// Order of the two 32-row halves of a staged block: 1 issues the second
+// half's products before the first half's exponentials (more overlap, more
+// registers), 0 runs the halves one after the other.  Per kernel: dQ, dK/dV.
+#ifndef FA2_BWD_PIPE_Q
+#define FA2_BWD_PIPE_Q 1
+#endif
+#ifndef FA2_BWD_PIPE_KV
+#define FA2_BWD_PIPE_KV 0
+#endif
 
 namespace fa2 {
 
@@ -49,25 +65,38 @@ __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Tile offsets (16-bit elements) of a 64-column row-major LDS tile whose
-// 16-byte chunks are swizzled by row % 8.
-//   row_ofs[dc]: A operand "rows x d" of MFMA chunk dc: lane reads row ql,
-//                chunk 2dc + h.
-//   tr_ofs[dt]:  A operand "d x rows" (transposed read): lane group i of 16
-//                gets 4 rows of column d; add 16c rows for chunk c and 8 rows
-//                for the upper half.
+// 16-byte chunk swizzle of the LDS tiles: logical chunk c of row r sits in
+// slot c ^ swz(r).  Tiles here are read both by rows (b128, 16 lanes per
+// pass: rows of one parity within 16 need distinct swz) and transposed
+// (tr_b16, 32 lanes per pass over 4 consecutive rows: rows r and r + 2 need
+// swz differing in bit 2).  j ^ 4(j & 1) with j = (r / 2) % 8 meets both.
+__device__ __forceinline__ int swz(int row) {
+    const int j = (row >> 1) & 7;
+    return j ^ ((j & 1) << 2);
+}
+
+// Tile offsets (16-bit elements) of a swizzled 64-column row-major LDS tile.
+//   row_ofs[dc]:  A operand "rows x d" of MFMA chunk dc: lane reads row ql,
+//                 chunk 2dc + h.
+//   tr_ofs[dt][u]: A operand "d x rows" (transposed read): lane group i of 16
+//                 gets 4 rows of column d, in rows kl (u = 0) and kl + 8
+//                 (u = 1); add 16c rows for contraction chunk c.
 struct TileOfs {
-    int row_ofs[4], tr_ofs[2];
+    int row_ofs[4], tr_ofs[2][2];
     __device__ __forceinline__ TileOfs(int lane) {
         const int h = lane >> 5, ql = lane & 31;
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) row_ofs[dc] = ql * kD + (((2 * dc + h) ^ (ql & 7)) << 3);
+        for (int dc = 0; dc < 4; ++dc) row_ofs[dc] = ql * kD + (((2 * dc + h) ^ swz(ql)) << 3);
         const int i = lane & 15;
         const int kl = 4 * h + (i >> 2);
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
             const int d = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
-            tr_ofs[dt] = kl * kD + (((d >> 3) ^ kl) << 3) + (d & 7);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int row = kl + 8 * u;
+                tr_ofs[dt][u] = row * kD + (((d >> 3) ^ swz(row)) << 3) + (d & 7);
+            }
         }
     }
 };
@@ -77,10 +106,9 @@ __device__ __forceinline__ u32x4 read_row(const uint16_t *tile, int ofs) {
 }
 
 // Transposed A operand for contraction chunk c (16 rows) and d tile dt.
-__device__ __forceinline__ u32x4 read_tr(const uint16_t *tile, int ofs, int c) {
-    const uint16_t *src = tile + ofs + 16 * c * kD;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 8 * kD));
+__device__ __forceinline__ u32x4 read_tr(const uint16_t *tile, const int *ofs, int c) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + ofs[0] + 16 * c * kD));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + ofs[1] + 16 * c * kD));
     const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
     const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
     return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -88,14 +116,14 @@ __device__ __forceinline__ u32x4 read_tr(const uint16_t *tile, int ofs, int c) {
 
 // HBM/L2 -> LDS of the 64 rows starting at row r0 of a [rows][64] tensor:
 // wave w moves 16-byte units [(2w+i)*64, +64); unit P holds chunk (P%8) ^
-// (row % 8) of row P/8.  Rows past the descriptor's range load nothing.
+// swz(row) of row P/8.  Rows past the descriptor's range load nothing.
 __device__ __forceinline__ void dma_tile(const __amdgpu_buffer_rsrc_t &r, uint16_t *dst, int r0,
                                          int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int unit = (2 * wave + i) * 64 + lane;
         const int row = unit >> 3;
-        const int ch = (unit & 7) ^ (row & 7);
+        const int ch = (unit & 7) ^ swz(row);
         const uint32_t off = (uint32_t)(((r0 + row) * kD + ch * 8) * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (2 * wave + i) * 512), 16, off,
                                                  0, 0, 0);
@@ -136,16 +164,20 @@ template <int DT, bool CAUSAL>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
-    uint16_t *__restrict__ dQ, int Nq, int Nk, float scale, float scale_log2) {
-    __shared__ __attribute__((aligned(16))) uint16_t sK0[kBlk * kD];
-    __shared__ __attribute__((aligned(16))) uint16_t sK1[kBlk * kD];
-    __shared__ __attribute__((aligned(16))) uint16_t sV0[kBlk * kD];
-    __shared__ __attribute__((aligned(16))) uint16_t sV1[kBlk * kD];
+    uint16_t *__restrict__ dQ, int BH, int Nq, int Nk, float scale, float scale_log2) {
+    // two buffers of 64 rows each for K and for V (block b in buffer b % 2)
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kBlk * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kBlk * kD];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, ql = lane & 31;
-    const int bh = blockIdx.y;
-    const int q0 = blockIdx.x * kRows;
+    // Workgroup w takes head w % BH and query block w / BH, counted from the
+    // last block when causal (the longest first).  Workgroups of one head are
+    // BH apart, a multiple of 8 when BH is, and so share one XCD's L2.
+    const int nqb = (Nq + kRows - 1) / kRows;
+    const int bh = blockIdx.x % BH;
+    const int qb = blockIdx.x / BH;
+    const int q0 = (CAUSAL ? nqb - 1 - qb : qb) * kRows;
     const int qw = q0 + 32 * wave;
     const int myq = qw + ql;
 
@@ -172,11 +204,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
     if (Nk % kBlk != 0) {  // rows past Nk are never loaded: keep them finite
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            reinterpret_cast<u32x4 *>(sK0)[tid + 256 * i] = z;
-            reinterpret_cast<u32x4 *>(sK1)[tid + 256 * i] = z;
-            reinterpret_cast<u32x4 *>(sV0)[tid + 256 * i] = z;
-            reinterpret_cast<u32x4 *>(sV1)[tid + 256 * i] = z;
+        for (int i = 0; i < 4; ++i) {
+            reinterpret_cast<u32x4 *>(sK)[tid + 256 * i] = z;
+            reinterpret_cast<u32x4 *>(sV)[tid + 256 * i] = z;
         }
         __syncthreads();
     }
@@ -185,17 +215,20 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[0][i] = acc[1][i] = 0.f;
 
-    // one 32-key tile (keys k0 .. k0+31 at rows 32T of the block)
-    auto tile = [&](int k0, const uint16_t *kt, const uint16_t *vt) {
-        if (CAUSAL && k0 > qw + 31) return;  // wholly above this wave's rows
-        f32x16 s = {}, dp = {};
+    // S^T and dP^T of one 32-key tile (rows kt / vt of the staged block):
+    // s[r], dp[r] belong to key k0 + 8(r/4) + 4h + r%4 and query myq.
+    auto prod = [&](const uint16_t *kt, const uint16_t *vt, f32x16 &s, f32x16 &dp) {
 #pragma unroll
         for (int dc = 0; dc < 4; ++dc) {
-            s = mma<DT>(read_row(kt, to.row_ofs[dc]), qf[dc], s);
-            dp = mma<DT>(read_row(vt, to.row_ofs[dc]), gf[dc], dp);
+            s = mma<DT>(read_row(kt, to.row_ofs[dc]), qf[dc], dc == 0 ? f32x16{} : s);
+            dp = mma<DT>(read_row(vt, to.row_ofs[dc]), gf[dc], dc == 0 ? f32x16{} : dp);
         }
-        // s[r], dp[r]: key k0 + 8(r/4) + 4h + r%4, query myq
-        u32x4 pk[2];
+    };
+    // dS^T = P^T o (dP^T - D), rounded and packed as the B operand of dQ^T.
+    // Keys past Nk and (causal) keys after the query get P = 0 when MASK.
+    auto softgrad = [&](auto mask_tag, int k0, const f32x16 &s, const f32x16 &dp, u32x4 *pk)
+        __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -204,24 +237,48 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int r = 8 * c + 2 * j + e;
-                    const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    bool live = qlive && key < Nk;
-                    if (CAUSAL) live = live && key <= myq;
-                    const float p = live ? exp2f_fast(__builtin_fmaf(s[r], scale_log2, -l2)) : 0.f;
-                    ds2[e] = p * (dp[r] - dlt);
+                    float x = __builtin_fmaf(s[r], scale_log2, -l2);
+                    if constexpr (MASK) {
+                        const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        bool live = key < Nk;
+                        if (CAUSAL) live = live && key <= myq;
+                        x = live ? x : -INFINITY;
+                    }
+                    ds2[e] = exp2f_fast(x) * (dp[r] - dlt);
                 }
                 pk[c][j] = pack2<DT>(ds2[0], ds2[1]);
             }
-        // dQ^T += K^T dS^T
+    };
+    // dQ^T += K^T dS^T (K^T by the transposed read of the staged keys)
+    auto grad = [&](const uint16_t *kt, const u32x4 *pk) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt) acc[dt] = mma<DT>(read_tr(kt, to.tr_ofs[dt], c), pk[c], acc[dt]);
     };
+    // One staged 64-key block: tiles A (keys kb..kb+31) and B (kb+32..).  B's
+    // products are issued before A's exponentials and A's dQ products before
+    // B's, so the matrix cores have work while the vector ALUs run.
+    auto compute = [&](auto mask_tag, int kb, const uint16_t *kc, const uint16_t *vc, bool doB) {
+        f32x16 sA, dA, sB, dB;
+        u32x4 pA[2], pB[2];
+        prod(kc, vc, sA, dA);
+        if (FA2_BWD_PIPE_Q && doB) prod(kc + 32 * kD, vc + 32 * kD, sB, dB);
+        softgrad(mask_tag, kb, sA, dA, pA);
+        grad(kc, pA);
+        if (doB) {
+            // keeps the scheduler from hoisting the second half's operand
+            // reads above the first half (which runs out of registers)
+            __builtin_amdgcn_sched_barrier(0);
+            if (!FA2_BWD_PIPE_Q) prod(kc + 32 * kD, vc + 32 * kD, sB, dB);
+            softgrad(mask_tag, kb + 32, sB, dB, pB);
+            grad(kc + 32 * kD, pB);
+        }
+    };
 
     if (nblk > 0) {
-        dma_tile(rk, sK0, 0, wave, lane);
-        dma_tile(rv, sV0, 0, wave, lane);
+        dma_tile(rk, sK, 0, wave, lane);
+        dma_tile(rv, sV, 0, wave, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
@@ -230,14 +287,23 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
             dma_tile(rk, kd, (b + 1) * kBlk, wave, lane);
             dma_tile(rv, vd, (b + 1) * kBlk, wave, lane);
         }
-        tile(b * kBlk, kc, vc);
-        tile(b * kBlk + 32, kc + 32 * kD, vc + 32 * kD);
+        const int kb = b * kBlk;
+        // causal: tiles wholly after this wave's last query are skipped
+        const bool doA = !CAUSAL || kb <= qw + 31;
+        const bool doB = !CAUSAL || kb + 32 <= qw + 31;
+        const bool mask = kb + kBlk > Nk || (CAUSAL && kb + kBlk - 1 > qw);
+        if (doA) {
+            if (mask)
+                compute(std::true_type{}, kb, kc, vc, doB);
+            else
+                compute(std::false_type{}, kb, kc, vc, true);
+        }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
-    for (int b = 0; b < nblk; b += 2) {
-        block(b, sK0, sV0, sK1, sV1);
-        if (b + 1 < nblk) block(b + 1, sK1, sV1, sK0, sV0);
+    for (int b = 0; b < nblk; ++b) {
+        const int cur = (b & 1) * kBlk * kD, nxt = kBlk * kD - cur;
+        block(b, sK + cur, sV + cur, sK + nxt, sV + nxt);
     }
 
     if (qlive) {
@@ -259,22 +325,22 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
 // dK, dV: a workgroup owns 128 keys (32 per wave) of one (b,h) and walks the
 // queries in 64-row tiles (Q, dO, L and D staged in LDS, double-buffered).
 template <int DT, bool CAUSAL>
-__global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kWaves * 64, FA2_BWD_KV_OCC) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
-    uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int Nq, int Nk, float scale,
+    uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int BH, int Nq, int Nk, float scale,
     float scale_log2) {
-    __shared__ __attribute__((aligned(16))) uint16_t sQ0[kBlk * kD];
-    __shared__ __attribute__((aligned(16))) uint16_t sQ1[kBlk * kD];
-    __shared__ __attribute__((aligned(16))) uint16_t sG0[kBlk * kD];
-    __shared__ __attribute__((aligned(16))) uint16_t sG1[kBlk * kD];
-    __shared__ __attribute__((aligned(16))) float sL0[2 * kBlk];  // L (base 2) then D of 64 rows
-    __shared__ __attribute__((aligned(16))) float sL1[2 * kBlk];
+    // two buffers of 64 rows each for Q, dO and (L, D) (tile t in buffer t % 2)
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[2 * kBlk * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t sG[2 * kBlk * kD];
+    __shared__ __attribute__((aligned(16))) float sL[2 * 2 * kBlk];  // L then D of 64 rows
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, ql = lane & 31;
-    const int bh = blockIdx.y;
-    const int k0 = blockIdx.x * kRows;
+    // Workgroup w takes head w % BH and key block w / BH (with causal masking
+    // the first key blocks see the most queries, so they start first).
+    const int bh = blockIdx.x % BH;
+    const int k0 = (blockIdx.x / BH) * kRows;
     const int kw = k0 + 32 * wave;  // first key of this wave
     const int myk = kw + ql;
 
@@ -302,16 +368,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_kernel(
     if (Nq % kBlk != 0) {  // rows past Nq are never loaded: keep them finite
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            reinterpret_cast<u32x4 *>(sQ0)[tid + 256 * i] = z;
-            reinterpret_cast<u32x4 *>(sQ1)[tid + 256 * i] = z;
-            reinterpret_cast<u32x4 *>(sG0)[tid + 256 * i] = z;
-            reinterpret_cast<u32x4 *>(sG1)[tid + 256 * i] = z;
+        for (int i = 0; i < 4; ++i) {
+            reinterpret_cast<u32x4 *>(sQ)[tid + 256 * i] = z;
+            reinterpret_cast<u32x4 *>(sG)[tid + 256 * i] = z;
         }
-        if (tid < 32) {
-            reinterpret_cast<u32x4 *>(sL0)[tid] = z;
-            reinterpret_cast<u32x4 *>(sL1)[tid] = z;
-        }
+        if (tid < 64) reinterpret_cast<u32x4 *>(sL)[tid] = z;
         __syncthreads();
     }
 
@@ -329,25 +390,30 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.f;
 
-    // one 32-query sub-tile: rows 32T of the staged tile (queries qa .. qa+31)
-    auto sub = [&](int qa, const uint16_t *qt, const uint16_t *gt, const float *sl) {
-        if (CAUSAL && qa + 31 < kw) return;  // every query before this wave's keys
-        f32x16 s = {}, dp = {};
+    // S and dP of one 32-query sub-tile (rows qt / gt of the staged tile):
+    // s[r], dp[r] belong to query qa + 8(r/4) + 4h + r%4 and key myk.
+    auto prod = [&](const uint16_t *qt, const uint16_t *gt, f32x16 &s, f32x16 &dp) {
 #pragma unroll
         for (int dc = 0; dc < 4; ++dc) {
-            s = mma<DT>(read_row(qt, to.row_ofs[dc]), kf[dc], s);
-            dp = mma<DT>(read_row(gt, to.row_ofs[dc]), vf[dc], dp);
+            s = mma<DT>(read_row(qt, to.row_ofs[dc]), kf[dc], dc == 0 ? f32x16{} : s);
+            dp = mma<DT>(read_row(gt, to.row_ofs[dc]), vf[dc], dc == 0 ? f32x16{} : dp);
         }
-        // s[r], dp[r]: query qa + 8(r/4) + 4h + r%4, key myk; L (to base 2)
-        // and D of those queries from the staged rows.
-        const int tb = qa - (qa & ~(kBlk - 1)) + 4 * h;  // staged row of r = 0
+    };
+    // P = exp(scale S - L) and dS = P o (dP - D), rounded and packed as the B
+    // operands of dV^T and dK^T.  With MASK, queries before the key get P = 0
+    // (causal); staged rows past Nq carry L = +inf and so P = 0 without a
+    // test.  L and D of the sub-tile's rows come from the staged tile: four
+    // consecutive rows per 16-byte read.
+    auto softgrad = [&](auto mask_tag, int qa, const float *sl, const f32x16 &s, const f32x16 &dp,
+                        u32x4 *pp, u32x4 *pd) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int tb = (qa & (kBlk - 1)) + 4 * h;  // staged row of r = 0
         f32x4 lq[4], dq4[4];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             lq[g4] = *reinterpret_cast<const f32x4 *>(sl + tb + 8 * g4) * kLog2e;
             dq4[g4] = *reinterpret_cast<const f32x4 *>(sl + kBlk + tb + 8 * g4);
         }
-        u32x4 pp[2], pd[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -356,18 +422,21 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_kernel(
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int r = 8 * c + 2 * j + e;
-                    const int q = qa + 8 * (r >> 2) + 4 * h + (r & 3);
-                    bool live = klive && q < Nq;
-                    if (CAUSAL) live = live && myk <= q;
-                    const float p =
-                        live ? exp2f_fast(__builtin_fmaf(s[r], scale_log2, -lq[r >> 2][r & 3])) : 0.f;
-                    pv[e] = p;
-                    dsv[e] = p * (dp[r] - dq4[r >> 2][r & 3]);
+                    float x = __builtin_fmaf(s[r], scale_log2, -lq[r >> 2][r & 3]);
+                    if constexpr (MASK) {
+                        const int q = qa + 8 * (r >> 2) + 4 * h + (r & 3);
+                        x = myk <= q ? x : -INFINITY;
+                    }
+                    pv[e] = exp2f_fast(x);
+                    dsv[e] = pv[e] * (dp[r] - dq4[r >> 2][r & 3]);
                 }
                 pp[c][j] = pack2<DT>(pv[0], pv[1]);
                 pd[c][j] = pack2<DT>(dsv[0], dsv[1]);
             }
-        // dV^T += dO^T P,  dK^T += Q^T dS (contraction over the 32 queries)
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 queries;
+    // dO^T and Q^T by the transposed read of the staged rows)
+    auto grad = [&](const uint16_t *qt, const uint16_t *gt, const u32x4 *pp, const u32x4 *pd) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -376,6 +445,27 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_kernel(
                 dk[dt] = mma<DT>(read_tr(qt, to.tr_ofs[dt], c), pd[c], dk[dt]);
             }
     };
+    // One staged 64-query tile: sub-tiles A (rows r0..r0+31) and B.  With
+    // causal masking A may lie wholly before this wave's keys (then only B
+    // runs).  B's products are issued before A's exponentials and A's
+    // gradient products before B's, so the matrix cores have work while the
+    // vector ALUs run.
+    auto compute = [&](auto mask_tag, int r0, const uint16_t *qc, const uint16_t *gc, const float *slc,
+                       bool doA) {
+        f32x16 sA, dA, sB, dB;
+        u32x4 pA[2], qA[2], pB[2], qB[2];
+        const uint16_t *qb = qc + 32 * kD, *gb = gc + 32 * kD;
+        if (doA) prod(qc, gc, sA, dA);
+        if (FA2_BWD_PIPE_KV) prod(qb, gb, sB, dB);
+        if (doA) {
+            softgrad(mask_tag, r0, slc, sA, dA, pA, qA);
+            grad(qc, gc, pA, qA);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // as in the dQ kernel
+        if (!FA2_BWD_PIPE_KV) prod(qb, gb, sB, dB);
+        softgrad(mask_tag, r0 + 32, slc, sB, dB, pB, qB);
+        grad(qb, gb, pB, qB);
+    };
 
     auto stage = [&](int t, uint16_t *qd, uint16_t *gd, float *sld) {
         const int r0 = qstart + t * kBlk;
@@ -383,23 +473,39 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_kernel(
         dma_tile(rdo, gd, r0, wave, lane);
         dma_ld(sld, r0);
     };
+    // After wave 0's copy of tile t's L has landed (its own wait), rows past
+    // Nq get L = +inf: their P is then exp(-inf) = 0 and dS = 0.  The barrier
+    // that follows publishes the write.
+    auto seal = [&](int t, float *sl) {
+        const int r0 = qstart + t * kBlk;
+        if (wave == 0 && r0 + kBlk > Nq && r0 + lane >= Nq) sl[lane] = INFINITY;
+    };
     if (ntile > 0) {
-        stage(0, sQ0, sG0, sL0);
+        stage(0, sQ, sG, sL);
         __builtin_amdgcn_s_waitcnt(0);
+        seal(0, sL);
         __syncthreads();
     }
     auto tile = [&](int t, const uint16_t *qc, const uint16_t *gc, const float *slc, uint16_t *qd,
                     uint16_t *gd, float *sld) {
         if (t + 1 < ntile) stage(t + 1, qd, gd, sld);
         const int r0 = qstart + t * kBlk;
-        sub(r0, qc, gc, slc);
-        sub(r0 + 32, qc + 32 * kD, gc + 32 * kD, slc);
+        const bool doA = !CAUSAL || r0 + 31 >= kw;
+        const bool doB = !CAUSAL || r0 + 63 >= kw;
+        if (doB) {
+            if (CAUSAL && r0 < kw + 31)  // some query of the tile is before some key
+                compute(std::true_type{}, r0, qc, gc, slc, doA);
+            else
+                compute(std::false_type{}, r0, qc, gc, slc, true);
+        }
         __builtin_amdgcn_s_waitcnt(0);
+        if (t + 1 < ntile) seal(t + 1, sld);
         __syncthreads();
     };
-    for (int t = 0; t < ntile; t += 2) {
-        tile(t, sQ0, sG0, sL0, sQ1, sG1, sL1);
-        if (t + 1 < ntile) tile(t + 1, sQ1, sG1, sL1, sQ0, sG0, sL0);
+    for (int t = 0; t < ntile; ++t) {
+        const int cur = (t & 1) * kBlk * kD, nxt = kBlk * kD - cur;
+        const int lcur = (t & 1) * 2 * kBlk, lnxt = 2 * kBlk - lcur;
+        tile(t, sQ + cur, sG + cur, sL + lcur, sQ + nxt, sG + nxt, sL + lnxt);
     }
 
     if (klive) {
@@ -433,14 +539,15 @@ fa2_status bwd_dt(const BwdArgs &a, hipStream_t st) {
         s = launch(bwd_delta_kernel<DT>, dim3((a.Nq + 31) / 32, bh), dim3(256), st, o, g, a.delta, a.Nq);
         if (s != FA2_OK) return s;
         auto kq = a.causal ? bwd_dq_kernel<DT, true> : bwd_dq_kernel<DT, false>;
-        s = launch(kq, dim3((a.Nq + kRows - 1) / kRows, bh), dim3(kWaves * 64), st, q, k, v, g, a.lse,
-                   (const float *)a.delta, (uint16_t *)a.dq, a.Nq, a.Nk, a.scale, sl2);
+        s = launch(kq, dim3((unsigned)((a.Nq + kRows - 1) / kRows) * bh), dim3(kWaves * 64), st, q, k, v,
+                   g, a.lse, (const float *)a.delta, (uint16_t *)a.dq, bh, a.Nq, a.Nk, a.scale, sl2);
         if (s != FA2_OK) return s;
     }
     // with no queries this still runs: it writes dK = dV = 0
     auto kk = a.causal ? bwd_dkdv_kernel<DT, true> : bwd_dkdv_kernel<DT, false>;
-    return launch(kk, dim3((a.Nk + kRows - 1) / kRows, bh), dim3(kWaves * 64), st, q, k, v, g, a.lse,
-                  (const float *)a.delta, (uint16_t *)a.dk, (uint16_t *)a.dv, a.Nq, a.Nk, a.scale, sl2);
+    return launch(kk, dim3((unsigned)((a.Nk + kRows - 1) / kRows) * bh), dim3(kWaves * 64), st, q, k,
+                  v, g, a.lse, (const float *)a.delta, (uint16_t *)a.dk, (uint16_t *)a.dv, bh, a.Nq,
+                  a.Nk, a.scale, sl2);
 }
 
 }  // namespace

@@ -76,8 +76,19 @@ constexpr float kLazyCap = 256.f;
 #ifndef FA2_SGB
 #define FA2_SGB 1
 #endif
+// FA2_VSWZ selects the V-tile swizzle (V is only read transposed, 32 lanes x
+// 8 bytes per pass over 4 consecutive keys): 1 = chunk ^ (j ^ 4(j % 2)) with
+// j = (key/2) % 8, under which keys k and k + 2 differ in bit 2 and the read
+// has no bank conflicts; 0 = chunk ^ (key % 8) (2-way conflicts).
+#ifndef FA2_VSWZ
+#define FA2_VSWZ 1
+#endif
 
 __device__ __forceinline__ int kswz(int key) { return FA2_KSWZ ? (key >> 1) & 7 : key & 7; }
+__device__ __forceinline__ int vswz(int key) {
+    const int j = (key >> 1) & 7;
+    return FA2_VSWZ ? j ^ ((j & 1) << 2) : key & 7;
+}
 
 // max over the two lanes l and l^32 of a wave (v_permlane32_swap exchanges the
 // halves of a register pair; either output pairing gives both halves).
@@ -193,14 +204,14 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
 
     // HBM/L2 -> LDS of the 64 rows starting at key k0: wave w moves 16-byte
     // units [(2w+i)*64, +64) of the block; unit P holds chunk (P%8) ^
-    // swizzle(row) of row P/8 (kswz for K, row % 8 for V).  Rows before key 0
+    // swizzle(row) of row P/8 (kswz for K, vswz for V).  Rows before key 0
     // or past Nk are out of the descriptor's range and load nothing.
     auto dma = [&](const __amdgpu_buffer_rsrc_t &r, uint16_t *dst, int k0, bool r_is_k) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int unit = (2 * wave + i) * 64 + lane;
             const int row = unit >> 3;
-            const int ch = (unit & 7) ^ (r_is_k ? kswz(row) : (row & 7));
+            const int ch = (unit & 7) ^ (r_is_k ? kswz(row) : vswz(row));
             const int key = k0 + row;
             const uint32_t off = key < 0 ? 0xFFFFFFF0u : (uint32_t)((key * kD + ch * 8) * 2);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (2 * wave + i) * 512), 16,
@@ -210,7 +221,7 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
 
     // LDS offsets that do not change from tile to tile (relative to the
     // tile's first row; both halves of a 64-row buffer share the swizzle).
-    int kofs[4], vofs[2];
+    int kofs[4], vofs[2][2];  // vofs[dt][u]: keys kl (u = 0) and kl + 8 (u = 1)
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) kofs[dc] = ql * kD + (((2 * dc + h) ^ kswz(ql)) << 3);
     {
@@ -219,7 +230,11 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
             const int d = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
-            vofs[dt] = kl * kD + (((d >> 3) ^ kl) << 3) + (d & 7);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int key = kl + 8 * u;
+                vofs[dt][u] = key * kD + (((d >> 3) ^ vswz(key)) << 3) + (d & 7);
+            }
         }
     }
 
@@ -259,9 +274,9 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt) {
-                const uint16_t *src = vt + vofs[dt] + 16 * c * kD;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)src);
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + 8 * kD));
+                const uint16_t *src = vt + 16 * c * kD;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + vofs[dt][0]));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + vofs[dt][1]));
                 const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
                 const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
                 vf[c][dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};

@@ -136,7 +136,8 @@ size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int causal, 
  *   that consume them (as P is in attn_fwd); delta, P and dS are formed in
  *   float32.  With Nq == 0, dk and dv are set to zero.
  *   Supported: D == 64; dtype F16, BF16 (F32 -> FA2_ERR_UNSUPPORTED); any
- *   B, H, Nq >= 0 (B*H == 0 enqueues nothing); Nk >= 1.
+ *   B, H, Nq >= 0 (B*H == 0 enqueues nothing); Nk >= 1; B*H*ceil(max(Nq,Nk)
+ *   / 128) < 2^24.
  */
 fa2_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
                     const void *dout, const float *lse, void *dq, void *dk, void *dv,
