@@ -15,7 +15,8 @@ Before the timed steps the multi-head f16/bf16 workload (B4 H12 M=N=2048
 D64, no LSE) and the causal f16 workload (Z1 H2 N1024, scale 0.5, with LSE,
 causal and not) are timed as the FlashAttention-2 README times its table
 (warm-up, then the median of 7 samples of 50 back-to-back calls, HIP events)
-and reported under ``extra`` (not part of ``value``).
+and reported under ``extra`` (not part of ``value``), as is the backward
+(attn_bwd) on the multi-head shape in f16 and bf16, and causal f16.
 
 The fp64 CPU oracle is timed on the host cores first (``cpu_baseline``): the
 whole headline workload, all 4096 rows, repeated for about three seconds.
@@ -208,6 +209,29 @@ def main():
                                                                      100 * tf / PEAK_F16))
             del q, k, v, o, lse
         del ws
+        # Backward on the multi-head shape: attn_bwd alone (O and the LSE from
+        # one untimed attn_fwd); 10*Nq*Nk*D flops per head (five products),
+        # halved when causal.
+        import dataclasses
+        from exact_attention_fa2_amd import inputs
+        for dt, causal in (("f16", False), ("bf16", False), ("f16", True)):
+            cfg = dataclasses.replace(workloads.multihead(2048, dt), causal=causal)
+            q, k, v = prefill_inputs(cfg)
+            g = upload(inputs.normal((cfg.B, cfg.H, cfg.Nq, cfg.D), cfg.seed, 3, dt), dt)
+            o, lse = fa2.attn_fwd(q, k, v, scale=cfg.scale, causal=causal, return_lse=True)
+            dq_, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            delta = torch.empty((cfg.B, cfg.H, cfg.Nq), dtype=torch.float32, device="cuda")
+            ms = time_median(lambda: fa2.attn_bwd(q, k, v, o, g, lse, scale=cfg.scale,
+                                                  causal=causal, dq=dq_, dk=dk_, dv=dv_,
+                                                  delta=delta), samples=7, calls=20)
+            fl = 2.5 * cfg.flops
+            tf = fl / (ms * 1e-3) / 1e12
+            name = "bwd %s%s" % (cfg.name, " causal" if causal else "")
+            extra[name] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 2),
+                           "frac_of_mfma_peak": round(tf / PEAK_F16, 4)}
+            log("%s: %.2f us, %.1f TFLOP/s (%.1f%% of MFMA peak)" % (name, ms * 1e3, tf,
+                                                                     100 * tf / PEAK_F16))
+            del q, k, v, g, o, lse, dq_, dk_, dv_, delta
         torch.cuda.empty_cache()
 
     pq, pk, pv = prefill_inputs(pre)

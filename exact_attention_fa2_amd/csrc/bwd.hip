@@ -28,9 +28,13 @@
 #include "fa2_device.h"
 #include "fa2_internal.h"
 
-// Waves per SIMD the dK/dV kernel is compiled for (its register budget).
+// Waves per SIMD the dK/dV kernel is compiled for (its register budget),
+// without and with causal masking.
 #ifndef FA2_BWD_KV_OCC
-#define FA2_BWD_KV_OCC 2
+#define FA2_BWD_KV_OCC 3
+#endif
+#ifndef FA2_BWD_KV_OCC_CAUSAL
+#define FA2_BWD_KV_OCC_CAUSAL 2
 #endif
 // Order of the two 32-row halves of a staged block: 1 issues the second
 // half's products before the first half's exponentials (more overlap, more
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
 // dK, dV: a workgroup owns 128 keys (32 per wave) of one (b,h) and walks the
 // queries in 64-row tiles (Q, dO, L and D staged in LDS, double-buffered).
 template <int DT, bool CAUSAL>
-__global__ __launch_bounds__(kWaves * 64, FA2_BWD_KV_OCC) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kWaves * 64, CAUSAL ? FA2_BWD_KV_OCC_CAUSAL : FA2_BWD_KV_OCC) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
     uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int BH, int Nq, int Nk, float scale,
@@ -351,12 +355,14 @@ __global__ __launch_bounds__(kWaves * 64, FA2_BWD_KV_OCC) void bwd_dkdv_kernel(
     const auto rl = make_rsrc(LSE + (size_t)bh * Nq, (uint32_t)Nq * 4);
     const auto rd = make_rsrc(Delta + (size_t)bh * Nq, (uint32_t)Nq * 4);
 
-    // B operands: chunk dc, slot (h, j) = X[myk][16dc + 8h + j]
+    // B operands: chunk dc, slot (h, j) = K[myk][16dc + 8h + j] and -V[..]
+    // (sign bits flipped, exact): the dP product then starts from D and
+    // yields D - dP, with the sign carried into the final scale of dK.
     u32x4 kf[4], vf[4];
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
         kf[dc] = load16(rk, (uint32_t)((myk * kD + 16 * dc + 8 * h) * 2));
-        vf[dc] = load16(rv, (uint32_t)((myk * kD + 16 * dc + 8 * h) * 2));
+        vf[dc] = load16(rv, (uint32_t)((myk * kD + 16 * dc + 8 * h) * 2)) ^ 0x80008000u;
     }
     const bool klive = myk < Nk;
 
@@ -390,30 +396,36 @@ __global__ __launch_bounds__(kWaves * 64, FA2_BWD_KV_OCC) void bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.f;
 
-    // S and dP of one 32-query sub-tile (rows qt / gt of the staged tile):
-    // s[r], dp[r] belong to query qa + 8(r/4) + 4h + r%4 and key myk.
-    auto prod = [&](const uint16_t *qt, const uint16_t *gt, f32x16 &s, f32x16 &dp) {
+    // S and D - dP of one 32-query sub-tile (rows qt / gt of the staged tile,
+    // L and D in sl): s[r], dn[r] belong to query qa + 8(r/4) + 4h + r%4 and
+    // key myk.  The second product starts from the staged D (four
+    // consecutive rows per 16-byte read land in four accumulator registers).
+    auto prod = [&](int qa, const uint16_t *qt, const uint16_t *gt, const float *sl, f32x16 &s,
+                    f32x16 &dn) {
+        const int tb = (qa & (kBlk - 1)) + 4 * h;  // staged row of r = 0
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sl + kBlk + tb + 8 * g4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dn[4 * g4 + i] = d4[i];
+        }
 #pragma unroll
         for (int dc = 0; dc < 4; ++dc) {
             s = mma<DT>(read_row(qt, to.row_ofs[dc]), kf[dc], dc == 0 ? f32x16{} : s);
-            dp = mma<DT>(read_row(gt, to.row_ofs[dc]), vf[dc], dc == 0 ? f32x16{} : dp);
+            dn = mma<DT>(read_row(gt, to.row_ofs[dc]), vf[dc], dn);
         }
     };
-    // P = exp(scale S - L) and dS = P o (dP - D), rounded and packed as the B
-    // operands of dV^T and dK^T.  With MASK, queries before the key get P = 0
-    // (causal); staged rows past Nq carry L = +inf and so P = 0 without a
-    // test.  L and D of the sub-tile's rows come from the staged tile: four
-    // consecutive rows per 16-byte read.
-    auto softgrad = [&](auto mask_tag, int qa, const float *sl, const f32x16 &s, const f32x16 &dp,
+    // P = exp2(c S - L log2 e) and -dS = P o (D - dP), rounded and packed as
+    // the B operands of dV^T and dK^T.  The staged L is already in base-2
+    // units, +inf on rows past Nq (P = 0 there without a test).  With MASK,
+    // queries before the key get P = 0 (causal).
+    auto softgrad = [&](auto mask_tag, int qa, const float *sl, const f32x16 &s, const f32x16 &dn,
                         u32x4 *pp, u32x4 *pd) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        const int tb = (qa & (kBlk - 1)) + 4 * h;  // staged row of r = 0
-        f32x4 lq[4], dq4[4];
+        const int tb = (qa & (kBlk - 1)) + 4 * h;
+        f32x4 lq[4];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            lq[g4] = *reinterpret_cast<const f32x4 *>(sl + tb + 8 * g4) * kLog2e;
-            dq4[g4] = *reinterpret_cast<const f32x4 *>(sl + kBlk + tb + 8 * g4);
-        }
+        for (int g4 = 0; g4 < 4; ++g4) lq[g4] = *reinterpret_cast<const f32x4 *>(sl + tb + 8 * g4);
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -428,7 +440,7 @@ __global__ __launch_bounds__(kWaves * 64, FA2_BWD_KV_OCC) void bwd_dkdv_kernel(
                         x = myk <= q ? x : -INFINITY;
                     }
                     pv[e] = exp2f_fast(x);
-                    dsv[e] = pv[e] * (dp[r] - dq4[r >> 2][r & 3]);
+                    dsv[e] = pv[e] * dn[r];
                 }
                 pp[c][j] = pack2<DT>(pv[0], pv[1]);
                 pd[c][j] = pack2<DT>(dsv[0], dsv[1]);
@@ -455,14 +467,14 @@ __global__ __launch_bounds__(kWaves * 64, FA2_BWD_KV_OCC) void bwd_dkdv_kernel(
         f32x16 sA, dA, sB, dB;
         u32x4 pA[2], qA[2], pB[2], qB[2];
         const uint16_t *qb = qc + 32 * kD, *gb = gc + 32 * kD;
-        if (doA) prod(qc, gc, sA, dA);
-        if (FA2_BWD_PIPE_KV) prod(qb, gb, sB, dB);
+        if (doA) prod(r0, qc, gc, slc, sA, dA);
+        if (FA2_BWD_PIPE_KV) prod(r0 + 32, qb, gb, slc, sB, dB);
         if (doA) {
             softgrad(mask_tag, r0, slc, sA, dA, pA, qA);
             grad(qc, gc, pA, qA);
         }
         __builtin_amdgcn_sched_barrier(0);  // as in the dQ kernel
-        if (!FA2_BWD_PIPE_KV) prod(qb, gb, sB, dB);
+        if (!FA2_BWD_PIPE_KV) prod(r0 + 32, qb, gb, slc, sB, dB);
         softgrad(mask_tag, r0 + 32, slc, sB, dB, pB, qB);
         grad(qb, gb, pB, qB);
     };
@@ -473,12 +485,12 @@ __global__ __launch_bounds__(kWaves * 64, FA2_BWD_KV_OCC) void bwd_dkdv_kernel(
         dma_tile(rdo, gd, r0, wave, lane);
         dma_ld(sld, r0);
     };
-    // After wave 0's copy of tile t's L has landed (its own wait), rows past
-    // Nq get L = +inf: their P is then exp(-inf) = 0 and dS = 0.  The barrier
-    // that follows publishes the write.
+    // After wave 0's copy of tile t's L has landed (its own wait), L goes to
+    // base-2 units and rows past Nq get L = +inf: their P is then exp2(-inf)
+    // = 0 and dS = 0.  The barrier that follows publishes the writes.
     auto seal = [&](int t, float *sl) {
         const int r0 = qstart + t * kBlk;
-        if (wave == 0 && r0 + kBlk > Nq && r0 + lane >= Nq) sl[lane] = INFINITY;
+        if (wave == 0) sl[lane] = r0 + lane < Nq ? sl[lane] * kLog2e : INFINITY;
     };
     if (ntile > 0) {
         stage(0, sQ, sG, sL);
@@ -509,6 +521,7 @@ __global__ __launch_bounds__(kWaves * 64, FA2_BWD_KV_OCC) void bwd_dkdv_kernel(
     }
 
     if (klive) {
+        const float nscale = -scale;  // the accumulated dS had its sign flipped
         uint16_t *krow = dK + ((size_t)bh * Nk + myk) * kD;
         uint16_t *vrow = dV + ((size_t)bh * Nk + myk) * kD;
 #pragma unroll
@@ -518,8 +531,8 @@ __global__ __launch_bounds__(kWaves * 64, FA2_BWD_KV_OCC) void bwd_dkdv_kernel(
                 const int r = 4 * g4;
                 const int d = 32 * dt + 8 * g4 + 4 * h;
                 u32x2 w;
-                w[0] = pack2<DT>(dk[dt][r] * scale, dk[dt][r + 1] * scale);
-                w[1] = pack2<DT>(dk[dt][r + 2] * scale, dk[dt][r + 3] * scale);
+                w[0] = pack2<DT>(dk[dt][r] * nscale, dk[dt][r + 1] * nscale);
+                w[1] = pack2<DT>(dk[dt][r + 2] * nscale, dk[dt][r + 3] * nscale);
                 *reinterpret_cast<u32x2 *>(krow + d) = w;
                 w[0] = pack2<DT>(dv[dt][r], dv[dt][r + 1]);
                 w[1] = pack2<DT>(dv[dt][r + 2], dv[dt][r + 3]);
