@@ -15,8 +15,9 @@ Before the timed steps the multi-head f16/bf16 workload (B4 H12 M=N=2048
 D64, no LSE) and the causal f16 workload (Z1 H2 N1024, scale 0.5, with LSE,
 causal and not) are timed as the FlashAttention-2 README times its table
 (warm-up, then the median of 7 samples of 50 back-to-back calls, HIP events)
-and reported under ``extra`` (not part of ``value``), as is the backward
-(attn_bwd) on the multi-head shape in f16 and bf16, and causal f16.
+and reported under ``extra`` (not part of ``value``), as are the generalised
+prefill shapes (D = 128 in f16 and bf16, a ragged N = 2000, Nq != Nk) and the
+backward (attn_bwd) on the multi-head shape in f16 and bf16, and causal f16.
 
 The fp64 CPU oracle is timed on the host cores first (``cpu_baseline``): the
 whole headline workload, all 4096 rows, repeated for about three seconds.
@@ -190,8 +191,15 @@ def main():
     extra = {}
     if not args.no_extra:
         ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
-        for cfg in (workloads.multihead(2048, "f16"), workloads.multihead(2048, "bf16"),
-                    workloads.causal_lse(True), workloads.causal_lse(False)):
+        # generalised prefill: head dimension 128, a ragged length, Nq != Nk
+        gen = [workloads.Prefill("B4 H12 M=N=2048 D128 %s" % dt, 4, 12, 2048, 2048, 128, dt,
+                                 1 / math.sqrt(128), False, 0) for dt in ("f16", "bf16")]
+        gen += [workloads.Prefill("B4 H12 M=N=2000 D64 f16 (ragged)", 4, 12, 2000, 2000, 64,
+                                  "f16", 0.125, False, 0),
+                workloads.Prefill("B4 H12 M=1024 N=4096 D64 f16", 4, 12, 1024, 4096, 64, "f16",
+                                  0.125, False, 0)]
+        for cfg in [workloads.multihead(2048, "f16"), workloads.multihead(2048, "bf16"),
+                    workloads.causal_lse(True), workloads.causal_lse(False)] + gen:
             q, k, v = prefill_inputs(cfg)
             o = torch.empty_like(q)
             with_lse = cfg.name.startswith("Z1")  # the causal workload's check includes the LSE

@@ -53,7 +53,7 @@ fa2_status fwd_impl(const void *q, const void *k, const void *v, void *o, float 
     if (B < 0 || H < 0 || Nq < 0 || Nk < 1 || D < 1) return FA2_ERR_SHAPE;
     if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
     if (causal != 0 && causal != 1) return FA2_ERR_UNSUPPORTED;
-    if (D != 64) return FA2_ERR_UNSUPPORTED;
+    if (D != 64 && !(D == 128 && dtype != FA2_F32)) return FA2_ERR_UNSUPPORTED;
     if (causal && Nq != Nk) return FA2_ERR_UNSUPPORTED;
     if ((long long)B * H * Nq == 0) return FA2_OK;  // nothing to compute
     if (!q || !k || !v || !o) return FA2_ERR_NULL;
@@ -66,11 +66,11 @@ fa2_status fwd_impl(const void *q, const void *k, const void *v, void *o, float 
     if ((long long)B * H > 65535) return FA2_ERR_UNSUPPORTED;
     const DeviceInfo *dev = current_device();
     if (!dev) return FA2_ERR_DEVICE;
-    fa2::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, scale, causal, dev->num_cus,
+    fa2::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dev->num_cus,
                    workspace, workspace ? workspace_bytes : 0};
     hipStream_t st = (hipStream_t)stream;
     if (dtype == FA2_F32) return fa2::launch_fwd_f32_d64(a, st);
-    return fa2::launch_fwd_mfma_d64(a, dtype, st);
+    return fa2::launch_fwd_mfma(a, dtype, st);
 }
 
 }  // namespace
@@ -91,13 +91,14 @@ FA2_API fa2_status attn_fwd_ws(const void *q, const void *k, const void *v, void
 
 FA2_API size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int causal,
                                        fa2_dtype dtype) {
-    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D != 64 || !valid_dtype(dtype)) return 0;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || !valid_dtype(dtype)) return 0;
+    if (D != 64 && !(D == 128 && dtype != FA2_F32)) return 0;
     if (causal && Nq != Nk) return 0;
     if ((long long)B * H > 65535) return 0;
     int cus = 256;
     if (const DeviceInfo *dev = current_device()) cus = dev->num_cus;
     if (dtype == FA2_F32) return fa2::f32_workspace_bytes(B, H, Nq, Nk, cus);
-    return fa2::mfma_workspace_bytes(B, H, Nq, Nk, causal, cus);
+    return fa2::mfma_workspace_bytes(B, H, Nq, Nk, D, causal, cus);
 }
 
 FA2_API fa2_status attn_bwd(const void *q, const void *k, const void *v, const void *o,

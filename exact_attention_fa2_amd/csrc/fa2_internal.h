@@ -19,7 +19,7 @@ struct FwdArgs {
     const void *q, *k, *v;
     void *o;
     float *lse;
-    int B, H, Nq, Nk;
+    int B, H, Nq, Nk, D;
     float scale;
     int causal;
     int num_cus;
@@ -29,8 +29,9 @@ struct FwdArgs {
 
 fa2_status launch_fwd_f32_d64(const FwdArgs &a, hipStream_t st);
 size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int num_cus);
-fa2_status launch_fwd_mfma_d64(const FwdArgs &a, fa2_dtype dt, hipStream_t st);
-size_t mfma_workspace_bytes(int B, int H, int Nq, int Nk, int causal, int num_cus);
+// f16/bf16 forward on matrix cores, D = 64 or 128.
+fa2_status launch_fwd_mfma(const FwdArgs &a, fa2_dtype dt, hipStream_t st);
+size_t mfma_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, int num_cus);
 
 struct BwdArgs {
     const void *q, *k, *v, *o, *dout;

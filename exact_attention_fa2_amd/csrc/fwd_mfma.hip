@@ -1,14 +1,15 @@
-// fwd_mfma.hip -- exact attention forward, f16 / bf16 in and out, D = 64, on
-// gfx950 matrix cores (v_mfma_f32_32x32x16_{f16,bf16}), f32 softmax state.
+// fwd_mfma.hip -- exact attention forward, f16 / bf16 in and out, D = 64 or
+// 128, on gfx950 matrix cores (v_mfma_f32_32x32x16_{f16,bf16}), f32 softmax
+// state.
 //
 // Method: the FlashAttention-2 forward ("Flash Attention" (aarnphm.xyz),
 // sections Deriving the online softmax and FlashAttention 2; "06: Fused
 // attention", attn_fwd).  A workgroup owns 128 query rows, one 32-row slab per
 // wave (each wave owns whole rows, so no cross-wave reduction is needed), and
 // walks the keys in blocks of 64 staged through LDS.  Per block and wave:
-//     S^T = K Q^T                    (8 MFMAs, f32 accumulate)
+//     S^T = K Q^T                    (D/8 MFMAs, f32 accumulate)
 //     m_new = max(m, rowmax S);  P = exp(S - m);  l = l*corr + rowsum P
-//     O^T = corr*O^T + V^T P^T       (8 MFMAs, P rounded to the input dtype)
+//     O^T = corr*O^T + V^T P^T       (D/8 MFMAs, P rounded to the input dtype)
 // After the last block O = O/l is rounded to the output dtype and
 // LSE = m + ln l is stored.  Causal: blocks wholly above the diagonal are never
 // loaded, blocks wholly above one wave's rows are skipped by that wave, and
@@ -39,14 +40,14 @@
 // 8*(r/4) + 4*(l/32) + r%4, column l%32):
 //   * S^T has keys as rows and queries as columns: lane l holds 32 scores of
 //     ONE query (l%32); its partner lane l^32 holds the other 32.
-//   * O^T likewise holds 32 of the 64 output columns of that query, so corr and
-//     1/l are per-lane scalars.
+//   * O^T likewise holds half of the D output columns of that query, so corr
+//     and 1/l are per-lane scalars.
 //   * The P registers feed the B operand of O^T = V^T P^T without moving:
 //     16-key chunk c of key tile T uses registers 8c..8c+7 of tile T.  The
 //     matching V^T operand comes from the row-major V block by the transposed
 //     LDS read (ds_read_b64_tr_b16): lane i of each 16-lane group receives 4
 //     keys of d = i when the group points at 4 keys x 4 groups of 4 columns.
-//   * LDS rows (128 bytes) have their 16-byte chunks XOR-swizzled by key.
+//   * LDS rows (2D bytes) have their 16-byte chunks XOR-swizzled by key.
 #include <algorithm>
 #include <type_traits>
 
@@ -57,7 +58,6 @@ namespace fa2 {
 
 namespace {
 
-constexpr int kD = 64;
 constexpr int kBR = 128;     // query rows per workgroup with one query group per wave
 constexpr int kBC = 64;      // keys per block
 constexpr int kWaves = 4;    // waves per workgroup
@@ -84,8 +84,18 @@ constexpr float kLazyCap = 256.f;
 #define FA2_VSWZ 1
 #endif
 
-__device__ __forceinline__ int kswz(int key) { return FA2_KSWZ ? (key >> 1) & 7 : key & 7; }
+// With D = 128 a row spans all 64 banks and both tiles use chunk ^ (4(key %
+// 4) + (key / 4) % 4): a permutation of the 16 chunks over any 16 keys (row
+// reads) that moves 4 consecutive keys to different aligned groups of four
+// chunks (transposed reads).
+template <int D>
+__device__ __forceinline__ int kswz(int key) {
+    if constexpr (D == 128) return ((key & 3) << 2) | ((key >> 2) & 3);
+    return FA2_KSWZ ? (key >> 1) & 7 : key & 7;
+}
+template <int D>
 __device__ __forceinline__ int vswz(int key) {
+    if constexpr (D == 128) return ((key & 3) << 2) | ((key >> 2) & 3);
     const int j = (key >> 1) & 7;
     return FA2_VSWZ ? j ^ ((j & 1) << 2) : key & 7;
 }
@@ -128,13 +138,21 @@ struct MfmaT<2> {
 // m_s (natural-log units), the denominator of the rounded P (lt, which
 // normalises O) and, with WLSE, that of the f32 P (l, for the LSE), and the
 // combine kernel merges them.
-template <int DT, bool CAUSAL, bool WLSE, bool SPLIT, int QG>
-__global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_kernel(
+// D: head dimension, 64 or 128 (128 only with QG = 1: its Q operand and O
+// accumulator take twice the registers, and its K/V buffers 64 KB of LDS).
+template <int D, int DT, bool CAUSAL, bool WLSE, bool SPLIT, int QG>
+__global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_mfma_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
     float *__restrict__ o_part, float *__restrict__ m_part, float *__restrict__ l_part,
     float *__restrict__ l2_part, int Nq, int Nk, float scale_log2, int n_qtiles, int n_tiles) {
-    constexpr int ROWS = kWaves * 32 * QG;  // query rows per workgroup
+    static_assert((D == 64 || D == 128) && (D == 64 || QG == 1), "head dimension");
+    constexpr int kD = D;
+    constexpr int NC = D / 16;                      // 16-wide contraction chunks of S^T = K Q^T
+    constexpr int NT = D / 32;                      // 32-column tiles of O^T
+    constexpr int CPR = D / 8;                      // 16-byte chunks per LDS row
+    constexpr int UPL = kBC * CPR / (kWaves * 64);  // 16-byte DMA units per lane per block
+    constexpr int ROWS = kWaves * 32 * QG;          // query rows per workgroup
     // Two K and two V buffers of 64 rows, as separate arrays (not one indexed
     // array) so the compiler can see that reads of one never alias DMA into
     // another.  V buffer b holds keys [64b, 64b + 64) of its block; K buffer b
@@ -170,11 +188,11 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
 
     // B operand of S^T = K Q^T for group g: chunk dc, slot (h, j) is
     // Q[qw + 32g + ql][16dc + 8h + j].
-    u32x4 qf[QG][4];
+    u32x4 qf[QG][NC];
 #pragma unroll
     for (int g = 0; g < QG; ++g)
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc)
+        for (int dc = 0; dc < NC; ++dc)
             qf[g][dc] = load16(rq, (uint32_t)(((qw + 32 * g + ql) * kD + 16 * dc + 8 * h) * 2));
 
     const int kend = CAUSAL ? min(Nk, q0 + ROWS) : Nk;
@@ -195,7 +213,7 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
     if (Nk % kBC != 0) {
         u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < UPL; ++i) {
             reinterpret_cast<u32x4 *>(sV0)[tid + 256 * i] = z;
             reinterpret_cast<u32x4 *>(sV1)[tid + 256 * i] = z;
         }
@@ -203,37 +221,37 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
     }
 
     // HBM/L2 -> LDS of the 64 rows starting at key k0: wave w moves 16-byte
-    // units [(2w+i)*64, +64) of the block; unit P holds chunk (P%8) ^
-    // swizzle(row) of row P/8 (kswz for K, vswz for V).  Rows before key 0
-    // or past Nk are out of the descriptor's range and load nothing.
+    // units [(UPL w + i) 64, +64) of the block; unit P holds chunk (P % CPR) ^
+    // swizzle(row) of row P / CPR (kswz for K, vswz for V).  Rows before key
+    // 0 or past Nk are out of the descriptor's range and load nothing.
     auto dma = [&](const __amdgpu_buffer_rsrc_t &r, uint16_t *dst, int k0, bool r_is_k) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int unit = (2 * wave + i) * 64 + lane;
-            const int row = unit >> 3;
-            const int ch = (unit & 7) ^ (r_is_k ? kswz(row) : vswz(row));
+        for (int i = 0; i < UPL; ++i) {
+            const int unit = (UPL * wave + i) * 64 + lane;
+            const int row = unit / CPR;
+            const int ch = (unit % CPR) ^ (r_is_k ? kswz<D>(row) : vswz<D>(row));
             const int key = k0 + row;
             const uint32_t off = key < 0 ? 0xFFFFFFF0u : (uint32_t)((key * kD + ch * 8) * 2);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (2 * wave + i) * 512), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (UPL * wave + i) * 512), 16,
                                                      off, 0, 0, 0);
         }
     };
 
     // LDS offsets that do not change from tile to tile (relative to the
     // tile's first row; both halves of a 64-row buffer share the swizzle).
-    int kofs[4], vofs[2][2];  // vofs[dt][u]: keys kl (u = 0) and kl + 8 (u = 1)
+    int kofs[NC], vofs[NT][2];  // vofs[dt][u]: keys kl (u = 0) and kl + 8 (u = 1)
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) kofs[dc] = ql * kD + (((2 * dc + h) ^ kswz(ql)) << 3);
+    for (int dc = 0; dc < NC; ++dc) kofs[dc] = ql * kD + (((2 * dc + h) ^ kswz<D>(ql)) << 3);
     {
         const int i = lane & 15;
         const int kl = 4 * h + (i >> 2);
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
+        for (int dt = 0; dt < NT; ++dt) {
             const int d = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int key = kl + 8 * u;
-                vofs[dt][u] = key * kD + (((d >> 3) ^ vswz(key)) << 3) + (d & 7);
+                vofs[dt][u] = key * kD + (((d >> 3) ^ vswz<D>(key)) << 3) + (d & 7);
             }
         }
     }
@@ -241,16 +259,15 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
     float m[QG], l[QG], lt[QG];  // per group: max used for the exponentials (base 2) and
                                  // this lane's halves of the denominators (f32 P, rounded P)
     const uint32_t ones = DT == 1 ? 0x3C003C00u : 0x3F803F80u;  // (1, 1) in f16 / bf16
-    f32x16 oacc[QG][2];
+    f32x16 oacc[QG][NT];
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
         m[g] = -INFINITY;
         l[g] = lt[g] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            oacc[g][0][i] = 0.f;
-            oacc[g][1][i] = 0.f;
-        }
+        for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[g][dt][i] = 0.f;
     }
 
     // One 32-key tile t.  On entry scur[g] holds S^T of tile t for group g
@@ -264,16 +281,16 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
         const int k0 = 32 * t;
         // All LDS operands of this tile, issued first so their latency is
         // covered by the exponentials.
-        u32x4 kf[4];
+        u32x4 kf[NC];
         if constexpr (NEXT) {
 #pragma unroll
-            for (int dc = 0; dc < 4; ++dc) kf[dc] = *reinterpret_cast<const u32x4 *>(&kn[kofs[dc]]);
+            for (int dc = 0; dc < NC; ++dc) kf[dc] = *reinterpret_cast<const u32x4 *>(&kn[kofs[dc]]);
         }
-        u32x4 vf[2][2];
+        u32x4 vf[2][NT];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt) {
+            for (int dt = 0; dt < NT; ++dt) {
                 const uint16_t *src = vt + 16 * c * kD;
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + vofs[dt][0]));
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + vofs[dt][1]));
@@ -312,9 +329,12 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
                     if constexpr (WLSE) ps[g][j & 1] += p0 + p1;
                     lp[g][j & 1] = dot2<DT>(w, ones, lp[g][j & 1]);
                     if constexpr (NEXT) {
-                        // scores of the next tile, one MFMA per exponential pair of chunk 0
-                        if (with_next && c == 0)
-                            snext[g] = MfmaT<DT>::mma(kf[j], qf[g][j], j == 0 ? f32x16{} : snext[g]);
+                        // scores of the next tile, one MFMA per exponential pair
+                        // of chunk 0 (D = 64) or of both chunks (D = 128)
+                        if (with_next && (NC == 8 || c == 0)) {
+                            const int jj = NC == 8 ? 4 * c + j : j;
+                            snext[g] = MfmaT<DT>::mma(kf[jj], qf[g][jj], jj == 0 ? f32x16{} : snext[g]);
+                        }
                     }
                 }
         };
@@ -329,8 +349,8 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
 #if FA2_SGB
         if constexpr (NEXT && QG == 1) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                __builtin_amdgcn_sched_group_barrier(0x002, WLSE ? 8 : 6, 0);
+            for (int j = 0; j < NC; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x002, (WLSE ? 32 : 24) / NC, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
         }
@@ -348,10 +368,9 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
                 l[g] *= corr;
                 lt[g] *= corr;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    oacc[g][0][i] *= corr;
-                    oacc[g][1][i] *= corr;
-                }
+                for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[g][dt][i] *= corr;
                 m[g] = m_new;
                 exps(g, m_use, false);
             }
@@ -361,7 +380,7 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
 #pragma unroll
             for (int g = 0; g < QG; ++g)
 #pragma unroll
-                for (int dt = 0; dt < 2; ++dt)
+                for (int dt = 0; dt < NT; ++dt)
                     oacc[g][dt] = MfmaT<DT>::mma(vf[c][dt], pk[g][c], oacc[g][dt]);
 #pragma unroll
         for (int g = 0; g < QG; ++g) {
@@ -411,7 +430,7 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
         __syncthreads();
         f32x16 sa[QG], sb[QG];
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) {
+        for (int dc = 0; dc < NC; ++dc) {
             const u32x4 a = *reinterpret_cast<const u32x4 *>(&sK1[32 * kD + kofs[dc]]);
 #pragma unroll
             for (int g = 0; g < QG; ++g) sa[g] = MfmaT<DT>::mma(a, qf[g][dc], dc == 0 ? f32x16{} : sa[g]);
@@ -433,9 +452,9 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
         if constexpr (WLSE) l[g] += __shfl_xor(l[g], 32);
     }
     if constexpr (SPLIT) {
-        // Partials: stage 32 rows x 64 columns at a time in LDS (each wave its
-        // own 8 KB buffer, free after the last barrier) so that each row's 256
-        // bytes go out as one contiguous piece.
+        // Partials: stage 32 rows x D columns at a time in LDS (each wave its
+        // own buffer of 64 D 2 bytes, free after the last barrier) so that each
+        // row's 4D bytes go out as one contiguous piece.
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         float *stage = reinterpret_cast<float *>(wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1);
@@ -444,7 +463,7 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
         for (int g = 0; g < QG; ++g) {
             const int myq = qw + 32 * g + ql;
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
+            for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int r = 4 * g4;
@@ -457,16 +476,21 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
                 l_part[pidx] = lt[g];
                 if constexpr (WLSE) l2_part[pidx] = l[g];
             }
-            // lane i of each 16-lane group writes 16 bytes of row 4j + lane/16
+            // lane i of each 16-lane group writes 16 bytes of row 4j + lane/16,
+            // columns 64 hc + 4 (lane % 16)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int row = 4 * j + (lane >> 4);
-                const int col = 4 * (lane & 15);
-                const int q = qw + 32 * g + row;
-                const f32x4 val = *reinterpret_cast<const f32x4 *>(stage + row * kD + (col ^ (4 * (row & 7))));
-                if (q < Nq)
-                    *reinterpret_cast<f32x4 *>(o_part + (((size_t)bh * Nq + q) * nch + blockIdx.y) * kD + col) = val;
-            }
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int hc = 0; hc < D / 64; ++hc) {
+                    const int row = 4 * j + (lane >> 4);
+                    const int col = 64 * hc + 4 * (lane & 15);
+                    const int q = qw + 32 * g + row;
+                    const f32x4 val =
+                        *reinterpret_cast<const f32x4 *>(stage + row * kD + (col ^ (4 * (row & 7))));
+                    if (q < Nq)
+                        *reinterpret_cast<f32x4 *>(o_part + (((size_t)bh * Nq + q) * nch + blockIdx.y) * kD +
+                                                   col) = val;
+                }
         }
         return;
     }
@@ -477,7 +501,7 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 ? 3 : 2) void fwd_mfma_d64_ker
             const float inv = 1.f / lt[g];
             uint16_t *orow = O + ((size_t)bh * Nq + myq) * kD;
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
+            for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int d = 32 * dt + 8 * g4 + 4 * h;
@@ -513,10 +537,10 @@ struct Plan {
 // when the query tiles fill at most an eighth of the compute units (with
 // more, writing and merging the partials costs more than the idle units),
 // into at most one chunk per two key blocks.
-Plan plan(int B, int H, int Nq, int Nk, int num_cus) {
+Plan plan(int B, int H, int Nq, int Nk, int D, int num_cus) {
     Plan p;
     p.qg = 1;
-    if (FA2_MFMA_QG2) {
+    if (FA2_MFMA_QG2 && D == 64) {
         const long long nt2 = (long long)((Nq + 2 * kBR - 1) / (2 * kBR)) * B * H;
         if (FA2_MFMA_QG2 == 2 || (nt2 >= 2LL * num_cus && nt2 % (2LL * num_cus) == 0)) p.qg = 2;
     }
@@ -534,62 +558,63 @@ Plan plan(int B, int H, int Nq, int Nk, int num_cus) {
 }
 
 size_t part_bytes(const FwdArgs &a, int chunks) {
-    return (size_t)a.B * a.H * a.Nq * chunks * (kD + 3) * sizeof(float);
+    return (size_t)a.B * a.H * a.Nq * chunks * (a.D + 3) * sizeof(float);
 }
 
-template <int DT, bool CAUSAL, bool WLSE, int QG>
+template <int D, int DT, bool CAUSAL, bool WLSE, int QG>
 fa2_status launch_q(const FwdArgs &a, const Plan &p, hipStream_t st) {
     const uint16_t *q = (const uint16_t *)a.q, *k = (const uint16_t *)a.k, *v = (const uint16_t *)a.v;
     const float sl2 = a.scale * kLog2e;
     if (p.chunks > 1 && a.ws && a.ws_bytes >= part_bytes(a, p.chunks)) {
         const size_t n = (size_t)a.B * a.H * a.Nq * p.chunks;
         float *o_part = (float *)a.ws;
-        float *m_part = o_part + n * kD;
+        float *m_part = o_part + n * D;
         float *l_part = m_part + n;
         float *l2_part = l_part + n;
-        fa2_status s = launch(fwd_mfma_d64_kernel<DT, CAUSAL, WLSE, true, QG>,
+        fa2_status s = launch(fwd_mfma_kernel<D, DT, CAUSAL, WLSE, true, QG>,
                               dim3((unsigned)p.n_tiles, (unsigned)p.chunks), dim3(kWaves * 64), st,
                               q, k, v, (uint16_t *)a.o, a.lse, o_part, m_part, l_part, l2_part, a.Nq,
                               a.Nk, sl2, p.n_qtiles, p.n_tiles);
         if (s != FA2_OK) return s;
-        return launch_combine_rows(o_part, m_part, l_part, a.o, a.lse, (size_t)a.B * a.H * a.Nq, kD,
+        return launch_combine_rows(o_part, m_part, l_part, a.o, a.lse, (size_t)a.B * a.H * a.Nq, D,
                                    p.chunks, DT == 1 ? FA2_F16 : FA2_BF16, st,
                                    WLSE ? l2_part : nullptr);
     }
-    return launch(fwd_mfma_d64_kernel<DT, CAUSAL, WLSE, false, QG>, dim3((unsigned)p.n_tiles),
+    return launch(fwd_mfma_kernel<D, DT, CAUSAL, WLSE, false, QG>, dim3((unsigned)p.n_tiles),
                   dim3(kWaves * 64), st, q, k, v, (uint16_t *)a.o, a.lse, (float *)nullptr,
                   (float *)nullptr, (float *)nullptr, (float *)nullptr, a.Nq, a.Nk, sl2,
                   p.n_qtiles, p.n_tiles);
 }
 
-template <int DT, bool CAUSAL, bool WLSE>
+template <int D, int DT, bool CAUSAL, bool WLSE>
 fa2_status launch_v(const FwdArgs &a, const Plan &p, hipStream_t st) {
-    if constexpr (FA2_MFMA_QG2 != 0) {
-        if (p.qg == 2) return launch_q<DT, CAUSAL, WLSE, 2>(a, p, st);
+    if constexpr (FA2_MFMA_QG2 != 0 && D == 64) {
+        if (p.qg == 2) return launch_q<D, DT, CAUSAL, WLSE, 2>(a, p, st);
     }
-    return launch_q<DT, CAUSAL, WLSE, 1>(a, p, st);
+    return launch_q<D, DT, CAUSAL, WLSE, 1>(a, p, st);
 }
 
-template <int DT>
+template <int D, int DT>
 fa2_status launch_dt(const FwdArgs &a, hipStream_t st) {
-    const Plan p = plan(a.B, a.H, a.Nq, a.Nk, a.num_cus);
+    const Plan p = plan(a.B, a.H, a.Nq, a.Nk, D, a.num_cus);
     if (p.n_tiles < 0) return FA2_ERR_UNSUPPORTED;
     if (a.causal)
-        return a.lse ? launch_v<DT, true, true>(a, p, st) : launch_v<DT, true, false>(a, p, st);
-    return a.lse ? launch_v<DT, false, true>(a, p, st) : launch_v<DT, false, false>(a, p, st);
+        return a.lse ? launch_v<D, DT, true, true>(a, p, st) : launch_v<D, DT, true, false>(a, p, st);
+    return a.lse ? launch_v<D, DT, false, true>(a, p, st) : launch_v<D, DT, false, false>(a, p, st);
 }
 
 }  // namespace
 
-fa2_status launch_fwd_mfma_d64(const FwdArgs &a, fa2_dtype dt, hipStream_t st) {
-    return dt == FA2_F16 ? launch_dt<1>(a, st) : launch_dt<2>(a, st);
+fa2_status launch_fwd_mfma(const FwdArgs &a, fa2_dtype dt, hipStream_t st) {
+    if (a.D == 128) return dt == FA2_F16 ? launch_dt<128, 1>(a, st) : launch_dt<128, 2>(a, st);
+    return dt == FA2_F16 ? launch_dt<64, 1>(a, st) : launch_dt<64, 2>(a, st);
 }
 
-size_t mfma_workspace_bytes(int B, int H, int Nq, int Nk, int causal, int num_cus) {
+size_t mfma_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, int num_cus) {
     (void)causal;
-    const Plan p = plan(B, H, Nq, Nk, num_cus);
+    const Plan p = plan(B, H, Nq, Nk, D, num_cus);
     if (p.chunks <= 1) return 0;
-    return (size_t)B * H * Nq * p.chunks * (kD + 3) * sizeof(float);
+    return (size_t)B * H * Nq * p.chunks * (D + 3) * sizeof(float);
 }
 
 }  // namespace fa2
