@@ -120,6 +120,57 @@ def decode_inputs(cfg):
     return out
 
 
+def extra_cases():
+    """The workloads reported under ``extra``, one at a time, as (name, call,
+    flops, info, calls per timing sample); each case's inputs are made when it
+    is reached and dropped after.
+
+    Forward: the multi-head f16/bf16 shape (no LSE), the causal f16 workload
+    (with LSE, causal and not), and the generalised prefill shapes (D = 128,
+    a ragged N = 2000, Nq != Nk).  Backward: attn_bwd alone on the multi-head
+    N = 2048 shape (O and the LSE from one untimed attn_fwd), 10*Nq*Nk*D flops
+    per head (five products), halved when causal."""
+    import dataclasses
+
+    import torch
+
+    from exact_attention_fa2_amd import fa2, inputs, workloads
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    fwd = [workloads.multihead(2048, "f16"), workloads.multihead(2048, "bf16"),
+           workloads.causal_lse(True), workloads.causal_lse(False)]
+    fwd += [workloads.Prefill("B4 H12 M=N=2048 D128 %s" % dt, 4, 12, 2048, 2048, 128, dt,
+                              1 / math.sqrt(128), False, 0) for dt in ("f16", "bf16")]
+    fwd += [workloads.Prefill("B4 H12 M=N=2000 D64 f16 (ragged)", 4, 12, 2000, 2000, 64, "f16",
+                              0.125, False, 0),
+            workloads.Prefill("B4 H12 M=1024 N=4096 D64 f16", 4, 12, 1024, 4096, 64, "f16",
+                              0.125, False, 0)]
+    for cfg in fwd:
+        q, k, v = prefill_inputs(cfg)
+        o = torch.empty_like(q)
+        with_lse = cfg.name.startswith("Z1")  # the causal workload's check includes the LSE
+        lse = torch.empty((cfg.B, cfg.H, cfg.Nq), dtype=torch.float32, device="cuda")
+        need = fa2.workspace_size(cfg.B, cfg.H, cfg.Nq, cfg.Nk, cfg.D, cfg.causal,
+                                  fa2.dtype_code(q))
+        assert need <= ws.numel()
+        yield (cfg.name, lambda: fa2.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o,
+                                              return_lse=with_lse, lse=lse, workspace=ws),
+               cfg.flops, {"lse": with_lse}, 50)
+        del q, k, v, o, lse
+    del ws
+    for dt, causal in (("f16", False), ("bf16", False), ("f16", True)):
+        cfg = dataclasses.replace(workloads.multihead(2048, dt), causal=causal)
+        q, k, v = prefill_inputs(cfg)
+        g = upload(inputs.normal((cfg.B, cfg.H, cfg.Nq, cfg.D), cfg.seed, 3, dt), dt)
+        o, lse = fa2.attn_fwd(q, k, v, scale=cfg.scale, causal=causal, return_lse=True)
+        dq_, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty((cfg.B, cfg.H, cfg.Nq), dtype=torch.float32, device="cuda")
+        yield ("bwd %s%s" % (cfg.name, " causal" if causal else ""),
+               lambda: fa2.attn_bwd(q, k, v, o, g, lse, scale=cfg.scale, causal=causal, dq=dq_,
+                                    dk=dk_, dv=dv_, delta=delta),
+               2.5 * cfg.flops, {}, 20)
+        del q, k, v, g, o, lse, dq_, dk_, dv_, delta
+
+
 def time_loop(fn, iters, warmup):
     """Mean kernel time (ms) of fn() over iters calls, events on the current stream."""
     import torch
@@ -153,6 +204,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--decode-dtype", default="f16", choices=["f16", "bf16"])
+    ap.add_argument("--profile-extra", default=None, metavar="PATTERN",
+                    help="only run the extra workloads whose name contains PATTERN, "
+                         "--profile-calls times each (for counter profiles), and exit")
+    ap.add_argument("--profile-calls", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (to scale the FETCH_SIZE "
                          "and WRITE_SIZE counters of a profile) and exit")
@@ -188,58 +243,28 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log("device: %s, %d CUs" % (props.name, props.multi_processor_count))
 
+    if args.profile_extra is not None:
+        # Counter runs: the matching extra workloads only, one call and then
+        # --profile-calls back-to-back calls each, no timing protocol.
+        for name, call, _, _, _ in extra_cases():
+            if args.profile_extra in name:
+                call()
+                torch.cuda.synchronize()
+                for _ in range(args.profile_calls):
+                    call()
+                torch.cuda.synchronize()
+                log("profiled %s" % name)
+        return
+
     extra = {}
     if not args.no_extra:
-        ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
-        # generalised prefill: head dimension 128, a ragged length, Nq != Nk
-        gen = [workloads.Prefill("B4 H12 M=N=2048 D128 %s" % dt, 4, 12, 2048, 2048, 128, dt,
-                                 1 / math.sqrt(128), False, 0) for dt in ("f16", "bf16")]
-        gen += [workloads.Prefill("B4 H12 M=N=2000 D64 f16 (ragged)", 4, 12, 2000, 2000, 64,
-                                  "f16", 0.125, False, 0),
-                workloads.Prefill("B4 H12 M=1024 N=4096 D64 f16", 4, 12, 1024, 4096, 64, "f16",
-                                  0.125, False, 0)]
-        for cfg in [workloads.multihead(2048, "f16"), workloads.multihead(2048, "bf16"),
-                    workloads.causal_lse(True), workloads.causal_lse(False)] + gen:
-            q, k, v = prefill_inputs(cfg)
-            o = torch.empty_like(q)
-            with_lse = cfg.name.startswith("Z1")  # the causal workload's check includes the LSE
-            lse = torch.empty((cfg.B, cfg.H, cfg.Nq), dtype=torch.float32, device="cuda")
-            need = fa2.workspace_size(cfg.B, cfg.H, cfg.Nq, cfg.Nk, cfg.D, cfg.causal,
-                                      fa2.dtype_code(q))
-            assert need <= ws.numel()
-            ms = time_median(lambda: fa2.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal,
-                                                  out=o, return_lse=with_lse, lse=lse,
-                                                  workspace=ws))
-            tf = cfg.flops / (ms * 1e-3) / 1e12
-            extra[cfg.name] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 2),
-                               "frac_of_mfma_peak": round(tf / PEAK_F16, 4), "lse": with_lse}
-            log("%s: %.2f us, %.1f TFLOP/s (%.1f%% of MFMA peak)" % (cfg.name, ms * 1e3, tf,
-                                                                     100 * tf / PEAK_F16))
-            del q, k, v, o, lse
-        del ws
-        # Backward on the multi-head shape: attn_bwd alone (O and the LSE from
-        # one untimed attn_fwd); 10*Nq*Nk*D flops per head (five products),
-        # halved when causal.
-        import dataclasses
-        from exact_attention_fa2_amd import inputs
-        for dt, causal in (("f16", False), ("bf16", False), ("f16", True)):
-            cfg = dataclasses.replace(workloads.multihead(2048, dt), causal=causal)
-            q, k, v = prefill_inputs(cfg)
-            g = upload(inputs.normal((cfg.B, cfg.H, cfg.Nq, cfg.D), cfg.seed, 3, dt), dt)
-            o, lse = fa2.attn_fwd(q, k, v, scale=cfg.scale, causal=causal, return_lse=True)
-            dq_, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-            delta = torch.empty((cfg.B, cfg.H, cfg.Nq), dtype=torch.float32, device="cuda")
-            ms = time_median(lambda: fa2.attn_bwd(q, k, v, o, g, lse, scale=cfg.scale,
-                                                  causal=causal, dq=dq_, dk=dk_, dv=dv_,
-                                                  delta=delta), samples=7, calls=20)
-            fl = 2.5 * cfg.flops
-            tf = fl / (ms * 1e-3) / 1e12
-            name = "bwd %s%s" % (cfg.name, " causal" if causal else "")
-            extra[name] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 2),
-                           "frac_of_mfma_peak": round(tf / PEAK_F16, 4)}
+        for name, call, flops, info, calls in extra_cases():
+            ms = time_median(call, calls=calls)
+            tf = flops / (ms * 1e-3) / 1e12
+            extra[name] = dict({"us": round(ms * 1e3, 2), "tflops": round(tf, 2),
+                                "frac_of_mfma_peak": round(tf / PEAK_F16, 4)}, **info)
             log("%s: %.2f us, %.1f TFLOP/s (%.1f%% of MFMA peak)" % (name, ms * 1e3, tf,
                                                                      100 * tf / PEAK_F16))
-            del q, k, v, g, o, lse, dq_, dk_, dv_, delta
         torch.cuda.empty_cache()
 
     pq, pk, pv = prefill_inputs(pre)

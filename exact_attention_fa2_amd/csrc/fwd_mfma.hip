@@ -531,6 +531,10 @@ struct Plan {
 #ifndef FA2_MFMA_QG2
 #define FA2_MFMA_QG2 1  // 1: 64 query rows per wave when the tiles fill the device twice over; 2: always
 #endif
+#ifndef FA2_MFMA_SPLIT_LONG
+#define FA2_MFMA_SPLIT_LONG 32  // also split when the tiles fill at most a quarter of the slots
+                                // and the keys span at least this many 64-key blocks (0: never)
+#endif
 
 // Query groups per wave: 64-row waves when the 256-row tiles make whole
 // rounds of two per compute unit.  Keys: split the keys of each query tile
@@ -548,11 +552,21 @@ Plan plan(int B, int H, int Nq, int Nk, int D, int num_cus) {
     const long long nt = (long long)p.n_qtiles * B * H;
     p.n_tiles = nt > 0x7FFFFFFF ? -1 : (int)nt;
     p.chunks = 1;
+    const long long nblk = (Nk + kBC - 1) / kBC;
     if (nt > 0 && nt * FA2_MFMA_SPLIT_BELOW <= num_cus) {
-        const long long nblk = (Nk + kBC - 1) / kBC;
         long long c = ((long long)FA2_MFMA_SPLIT_WGS * num_cus + nt - 1) / nt;
         c = std::min<long long>(c, std::max<long long>(1, nblk / 2));
         p.chunks = (int)std::min<long long>(c, 32);
+    } else if (FA2_MFMA_SPLIT_LONG > 0 && nt > 0 && nblk >= FA2_MFMA_SPLIT_LONG) {
+        // Long keys with the tiles filling at most a quarter of the resident
+        // workgroup slots: cut the keys so the chunks fill the slots (the
+        // partials then cost little next to the work of each chunk; at half
+        // the slots writing them costs more than the idle slots).
+        const long long slots = (long long)num_cus * (p.qg == 1 && D == 64 ? 3 : 2);
+        if (4 * nt <= slots) {
+            const long long c = std::min<long long>(slots / nt, nblk / 16);
+            p.chunks = (int)std::max<long long>(1, std::min<long long>(c, 32));
+        }
     }
     return p;
 }

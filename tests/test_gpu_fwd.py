@@ -230,12 +230,15 @@ def test_f32_schedules(shape, causal):
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", [(1, 2, 1024, 1024, True), (1, 2, 1024, 1024, False),
                                    (1, 1, 700, 700, True), (2, 3, 300, 300, False),
-                                   (1, 1, 64, 4096, False), (1, 3, 129, 2000, False)],
+                                   (1, 1, 64, 4096, False), (1, 3, 129, 2000, False),
+                                   (1, 4, 4096, 4096, True), (1, 2, 2048, 8192, False)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_mfma_split_schedules(shape, dt):
     """f16/bf16 with few query tiles: the keys are split across workgroups
     (workspace + combine) or not (no workspace); both against the oracle, O
-    and LSE."""
+    and LSE.  The last two shapes fill more than an eighth of the compute
+    units but at most a quarter of the workgroup slots, with long keys: the
+    second split rule."""
     import torch
     B, H, Nq, Nk, causal = shape
     q, k, v = seeded(B, H, Nq, Nk, 64, dt, 13)

@@ -53,7 +53,8 @@ def test_ragged_and_degenerate(shape, dt):
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", [(1, 2, 1024, 1024, True), (1, 2, 1024, 1024, False),
-                                   (1, 1, 64, 4096, False), (1, 3, 129, 2000, False)],
+                                   (1, 1, 64, 4096, False), (1, 3, 129, 2000, False),
+                                   (1, 2, 4096, 4096, True)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_split_schedules(shape, dt):
     """Few query tiles: keys split across workgroups with a workspace (partials
