@@ -140,3 +140,48 @@ def test_bwd_rejects():
     with pytest.raises(fa2.FA2Error) as e:
         fa2.attn_bwd(h, h, h, h, h, lse)
     assert e.value.status == 3
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_bwd_deterministic(dt):
+    """No atomics: two runs give the same bits."""
+    import torch
+    q, k, v = inputs.qkv((2, 3, 300, 64), (2, 3, 300, 64), 6, dt)
+    g = inputs.normal((2, 3, 300, 64), 6, 3, dt)
+    tq, tk, tv, tg = (upload(x, dt) for x in (q, k, v, g))
+    o, lse = fa2.attn_fwd(tq, tk, tv, scale=0.125, causal=True, return_lse=True)
+    a = fa2.attn_bwd(tq, tk, tv, o, tg, lse, scale=0.125, causal=True)
+    b = fa2.attn_bwd(tq, tk, tv, o, tg, lse, scale=0.125, causal=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_bwd_offsets_past_2_31_elements(dt):
+    """B*H = 8192 heads of N = 4096: each [B,H,N,64] tensor holds 2^31
+    elements (4 GiB), so the last heads sit past any 32-bit element offset.
+    Q = K = 0 makes every P exactly 2^-12; with dO and V in {-1, +1} the
+    gradients are exact: dQ = dK = 0 and dV_j = 2^-12 sum_q dO_q for every key
+    j (a sum of 4096 terms of +-1, exact in float32).  Checked in full for the
+    first, a middle and the last heads, and dQ = dK = 0 everywhere."""
+    import torch
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    B, H, N = 128, 64, 4096
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    shape = (B, H, N, 64)
+    q = torch.zeros(shape, device="cuda", dtype=tdt)
+    k = torch.zeros(shape, device="cuda", dtype=tdt)
+    v = (torch.randint(0, 2, shape, device="cuda", generator=gen, dtype=torch.int8) * 2 - 1).to(tdt)
+    g = (torch.randint(0, 2, shape, device="cuda", generator=gen, dtype=torch.int8) * 2 - 1).to(tdt)
+    o, lse = fa2.attn_fwd(q, k, v, scale=0.125, return_lse=True)
+    dq, dk, dv, _ = fa2.attn_bwd(q, k, v, o, g, lse, scale=0.125)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dq).item() == 0
+    assert torch.count_nonzero(dk).item() == 0
+    gf = g.view(B * H, N, 64)
+    dvf = dv.view(B * H, N, 64)
+    for head in (0, B * H // 2 + 3, B * H - 1):
+        # the exact value, rounded to the output dtype as the kernel rounds its exact f32 sum
+        want = (gf[head].double().sum(dim=0) / N).to(tdt).double()
+        got = dvf[head].double()
+        assert torch.equal(got, want.expand_as(got)), head
