@@ -128,8 +128,9 @@ def extra_cases():
     Forward: the multi-head f16/bf16 shape (no LSE), the causal f16 workload
     (with LSE, causal and not), and the generalised prefill shapes (D = 128,
     a ragged N = 2000, Nq != Nk).  Backward: attn_bwd alone on the multi-head
-    N = 2048 shape (O and the LSE from one untimed attn_fwd), 10*Nq*Nk*D flops
-    per head (five products), halved when causal."""
+    N = 2048 shape (f16, bf16, causal f16, and f16 at D = 128; O and the LSE
+    from one untimed attn_fwd), 10*Nq*Nk*D flops per head (five products),
+    halved when causal."""
     import dataclasses
 
     import torch
@@ -157,8 +158,12 @@ def extra_cases():
                cfg.flops, {"lse": with_lse}, 50)
         del q, k, v, o, lse
     del ws
-    for dt, causal in (("f16", False), ("bf16", False), ("f16", True)):
-        cfg = dataclasses.replace(workloads.multihead(2048, dt), causal=causal)
+    bwd = [dataclasses.replace(workloads.multihead(2048, dt), causal=causal)
+           for dt, causal in (("f16", False), ("bf16", False), ("f16", True))]
+    bwd.append(workloads.Prefill("B4 H12 M=N=2048 D128 f16", 4, 12, 2048, 2048, 128, "f16",
+                                 1 / math.sqrt(128), False, 0))
+    for cfg in bwd:
+        dt, causal = cfg.dtype, cfg.causal
         q, k, v = prefill_inputs(cfg)
         g = upload(inputs.normal((cfg.B, cfg.H, cfg.Nq, cfg.D), cfg.seed, 3, dt), dt)
         o, lse = fa2.attn_fwd(q, k, v, scale=cfg.scale, causal=causal, return_lse=True)

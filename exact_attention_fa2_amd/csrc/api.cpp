@@ -108,7 +108,7 @@ FA2_API fa2_status attn_bwd(const void *q, const void *k, const void *v, const v
     if (B < 0 || H < 0 || Nq < 0 || Nk < 1 || D < 1) return FA2_ERR_SHAPE;
     if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
     if (causal != 0 && causal != 1) return FA2_ERR_UNSUPPORTED;
-    if (D != 64 || dtype == FA2_F32) return FA2_ERR_UNSUPPORTED;
+    if ((D != 64 && D != 128) || dtype == FA2_F32) return FA2_ERR_UNSUPPORTED;
     if (causal && Nq != Nk) return FA2_ERR_UNSUPPORTED;
     if ((long long)B * H == 0) return FA2_OK;
     if (!k || !v || !dk || !dv) return FA2_ERR_NULL;
@@ -120,11 +120,14 @@ FA2_API fa2_status attn_bwd(const void *q, const void *k, const void *v, const v
     if ((long long)Nk * D * es > kMaxSliceBytes || (long long)Nq * D * es > kMaxSliceBytes)
         return FA2_ERR_UNSUPPORTED;
     if ((long long)B * H > 65535) return FA2_ERR_UNSUPPORTED;
-    // one workgroup per 128 rows of each (b,h): the grid holds fewer than 2^24
-    if ((long long)((Nq > Nk ? Nq : Nk) + 127) / 128 * B * H >= (1LL << 24)) return FA2_ERR_UNSUPPORTED;
+    // one workgroup per 128 query rows or per 128 keys (64 with D = 128) of
+    // each (b,h): the grids hold fewer than 2^24 workgroups
+    const int per_wg = D == 64 ? 128 : 64;
+    if ((long long)((Nq > Nk ? Nq : Nk) + per_wg - 1) / per_wg * B * H >= (1LL << 24))
+        return FA2_ERR_UNSUPPORTED;
     if (!current_device()) return FA2_ERR_DEVICE;
-    fa2::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, scale, causal};
-    return fa2::launch_bwd_mfma_d64(a, dtype, (hipStream_t)stream);
+    fa2::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, D, scale, causal};
+    return fa2::launch_bwd_mfma(a, dtype, (hipStream_t)stream);
 }
 
 FA2_API fa2_status attn_decode_split(const void *q, const void *k, const void *v,

@@ -1,5 +1,5 @@
-// bwd.hip -- exact attention backward, f16 / bf16, D = 64, on gfx950 matrix
-// cores, float32 accumulation.
+// bwd.hip -- exact attention backward, f16 / bf16, D = 64 or 128, on gfx950
+// matrix cores, float32 accumulation.
 //
 // Method ("Flash Attention" (aarnphm.xyz), section IO complexity, the
 // paragraph on the backward pass; "06: Fused attention", the backward
@@ -9,7 +9,8 @@
 //     dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D_i),
 //     dQ = scale dS K,   dK = scale dS^T Q.
 // Three kernels: D (one pass over O and dO), dQ (a workgroup per 128 query
-// rows walking the keys), dK/dV (a workgroup per 128 keys walking the
+// rows walking the keys), dK/dV (a workgroup per 128 keys -- 64 with D = 128,
+// where two waves share 32 keys and split the output columns -- walking the
 // queries).  P and dS are rounded to the input dtype before their MFMAs, as
 // P is in the forward.
 //
@@ -50,7 +51,6 @@ namespace fa2 {
 
 namespace {
 
-constexpr int kD = 64;
 constexpr int kWaves = 4;
 constexpr int kRows = 128;  // rows (queries or keys) a workgroup owns: 32 per wave
 constexpr int kBlk = 64;    // rows of the other side staged per block
@@ -71,35 +71,42 @@ __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
 
 // 16-byte chunk swizzle of the LDS tiles: logical chunk c of row r sits in
 // slot c ^ swz(r).  Tiles here are read both by rows (b128, 16 lanes per
-// pass: rows of one parity within 16 need distinct swz) and transposed
-// (tr_b16, 32 lanes per pass over 4 consecutive rows: rows r and r + 2 need
-// swz differing in bit 2).  j ^ 4(j & 1) with j = (r / 2) % 8 meets both.
+// pass) and transposed (tr_b16, 32 lanes per pass over 4 consecutive rows).
+// D = 64 (128-byte rows, two per 64 banks): rows of one parity within 16 need
+// distinct swz, rows r and r + 2 swz differing in bit 2; j ^ 4(j & 1) with
+// j = (r / 2) % 8 meets both.  D = 128 (a row spans the 64 banks): swz must
+// permute 16 chunks over any 16 rows and send 4 consecutive rows to different
+// aligned groups of four; 4(r % 4) + (r / 4) % 4 does.
+template <int D>
 __device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
     const int j = (row >> 1) & 7;
     return j ^ ((j & 1) << 2);
 }
 
-// Tile offsets (16-bit elements) of a swizzled 64-column row-major LDS tile.
+// Tile offsets (16-bit elements) of a swizzled D-column row-major LDS tile.
 //   row_ofs[dc]:  A operand "rows x d" of MFMA chunk dc: lane reads row ql,
 //                 chunk 2dc + h.
-//   tr_ofs[dt][u]: A operand "d x rows" (transposed read): lane group i of 16
-//                 gets 4 rows of column d, in rows kl (u = 0) and kl + 8
-//                 (u = 1); add 16c rows for contraction chunk c.
+//   tr_ofs[dt][u]: A operand "d x rows" (transposed read) of the 32 columns
+//                 from dbase + 32 dt: lane group i of 16 gets 4 rows of
+//                 column d, in rows kl (u = 0) and kl + 8 (u = 1); add 16c
+//                 rows for contraction chunk c.
+template <int D, int NTR>
 struct TileOfs {
-    int row_ofs[4], tr_ofs[2][2];
-    __device__ __forceinline__ TileOfs(int lane) {
+    int row_ofs[D / 16], tr_ofs[NTR][2];
+    __device__ __forceinline__ TileOfs(int lane, int dbase) {
         const int h = lane >> 5, ql = lane & 31;
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) row_ofs[dc] = ql * kD + (((2 * dc + h) ^ swz(ql)) << 3);
+        for (int dc = 0; dc < D / 16; ++dc) row_ofs[dc] = ql * D + (((2 * dc + h) ^ swz<D>(ql)) << 3);
         const int i = lane & 15;
         const int kl = 4 * h + (i >> 2);
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-            const int d = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+        for (int dt = 0; dt < NTR; ++dt) {
+            const int d = dbase + 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int row = kl + 8 * u;
-                tr_ofs[dt][u] = row * kD + (((d >> 3) ^ swz(row)) << 3) + (d & 7);
+                tr_ofs[dt][u] = row * D + (((d >> 3) ^ swz<D>(row)) << 3) + (d & 7);
             }
         }
     }
@@ -110,39 +117,45 @@ __device__ __forceinline__ u32x4 read_row(const uint16_t *tile, int ofs) {
 }
 
 // Transposed A operand for contraction chunk c (16 rows) and d tile dt.
+template <int D>
 __device__ __forceinline__ u32x4 read_tr(const uint16_t *tile, const int *ofs, int c) {
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + ofs[0] + 16 * c * kD));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + ofs[1] + 16 * c * kD));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + ofs[0] + 16 * c * D));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(tile + ofs[1] + 16 * c * D));
     const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
     const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
     return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
 }
 
-// HBM/L2 -> LDS of the 64 rows starting at row r0 of a [rows][64] tensor:
-// wave w moves 16-byte units [(2w+i)*64, +64); unit P holds chunk (P%8) ^
-// swz(row) of row P/8.  Rows past the descriptor's range load nothing.
+// HBM/L2 -> LDS of the 64 rows starting at row r0 of a [rows][D] tensor:
+// wave w moves 16-byte units [(U w + i) 64, +64), U = D / 32; unit P holds
+// chunk (P % (D/8)) ^ swz(row) of row P / (D/8).  Rows past the descriptor's
+// range load nothing.
+template <int D>
 __device__ __forceinline__ void dma_tile(const __amdgpu_buffer_rsrc_t &r, uint16_t *dst, int r0,
                                          int wave, int lane) {
+    constexpr int U = D / 32, CPR = D / 8;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int unit = (2 * wave + i) * 64 + lane;
-        const int row = unit >> 3;
-        const int ch = (unit & 7) ^ swz(row);
-        const uint32_t off = (uint32_t)(((r0 + row) * kD + ch * 8) * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (2 * wave + i) * 512), 16, off,
+    for (int i = 0; i < U; ++i) {
+        const int unit = (U * wave + i) * 64 + lane;
+        const int row = unit / CPR;
+        const int ch = (unit % CPR) ^ swz<D>(row);
+        const uint32_t off = (uint32_t)(((r0 + row) * D + ch * 8) * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (U * wave + i) * 512), 16, off,
                                                  0, 0, 0);
     }
 }
 
 // ---------------------------------------------------------------------------
-// D_i = sum_d dO_id O_id, float32; 8 lanes per row, each 16 bytes.  Grid:
-// (ceil(Nq / 32), B*H).
-template <int DT>
+// D_i = sum_d dO_id O_id, float32; D/8 lanes per row, each 16 bytes.  Grid:
+// (ceil(Nq / (256 / (D/8))), B*H).
+template <int D, int DT>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restrict__ O,
                                                         const uint16_t *__restrict__ dO,
                                                         float *__restrict__ Delta, int Nq) {
-    const int row = (blockIdx.x * 256 + threadIdx.x) >> 3;
-    const int c = threadIdx.x & 7;
+    constexpr int LPR = D / 8;
+    constexpr int kD = D;
+    const int row = (blockIdx.x * 256 + threadIdx.x) / LPR;
+    const int c = threadIdx.x % LPR;
     const size_t base = (size_t)blockIdx.y * Nq;
     float acc = 0.f;
     if (row < Nq) {
@@ -157,18 +170,20 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restri
             acc = __builtin_fmaf(a1, b1, acc);
         }
     }
-    acc = group_reduce<8>(acc);
+    acc = group_reduce<LPR>(acc);
     if (row < Nq && c == 0) Delta[base + row] = acc;
 }
 
 // ---------------------------------------------------------------------------
 // dQ: a workgroup owns 128 query rows (32 per wave) of one (b,h) and walks
 // the keys in 64-key blocks (K and V double-buffered in LDS).
-template <int DT, bool CAUSAL>
+template <int D, int DT, bool CAUSAL>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
     uint16_t *__restrict__ dQ, int BH, int Nq, int Nk, float scale, float scale_log2) {
+    constexpr int kD = D, NC = D / 16, NT = D / 32;
+    constexpr bool PIPE = FA2_BWD_PIPE_Q && D == 64;  // D = 128 has no registers for it
     // two buffers of 64 rows each for K and for V (block b in buffer b % 2)
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kBlk * kD];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kBlk * kD];
@@ -191,9 +206,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
     const auto rv = make_rsrc(V + (size_t)bh * Nk * kD, (uint32_t)Nk * kD * 2);
 
     // B operands: chunk dc, slot (h, j) = X[myq][16dc + 8h + j]
-    u32x4 qf[4], gf[4];
+    u32x4 qf[NC], gf[NC];
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
+    for (int dc = 0; dc < NC; ++dc) {
         qf[dc] = load16(rq, (uint32_t)((myq * kD + 16 * dc + 8 * h) * 2));
         gf[dc] = load16(rdo, (uint32_t)((myq * kD + 16 * dc + 8 * h) * 2));
     }
@@ -203,27 +218,29 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
 
     const int kend = CAUSAL ? min(Nk, q0 + kRows) : Nk;
     const int nblk = (kend + kBlk - 1) / kBlk;
-    const TileOfs to(lane);
+    const TileOfs<D, NT> to(lane, 0);
 
     if (Nk % kBlk != 0) {  // rows past Nk are never loaded: keep them finite
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < D / 16; ++i) {
             reinterpret_cast<u32x4 *>(sK)[tid + 256 * i] = z;
             reinterpret_cast<u32x4 *>(sV)[tid + 256 * i] = z;
         }
         __syncthreads();
     }
 
-    f32x16 acc[2];  // dQ^T: acc[dt][r] = dQ[myq][32dt + 8(r/4) + 4h + r%4] / scale
+    f32x16 acc[NT];  // dQ^T: acc[dt][r] = dQ[myq][32dt + 8(r/4) + 4h + r%4] / scale
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[0][i] = acc[1][i] = 0.f;
+    for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
     // S^T and dP^T of one 32-key tile (rows kt / vt of the staged block):
     // s[r], dp[r] belong to key k0 + 8(r/4) + 4h + r%4 and query myq.
     auto prod = [&](const uint16_t *kt, const uint16_t *vt, f32x16 &s, f32x16 &dp) {
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) {
+        for (int dc = 0; dc < NC; ++dc) {
             s = mma<DT>(read_row(kt, to.row_ofs[dc]), qf[dc], dc == 0 ? f32x16{} : s);
             dp = mma<DT>(read_row(vt, to.row_ofs[dc]), gf[dc], dc == 0 ? f32x16{} : dp);
         }
@@ -258,7 +275,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt) acc[dt] = mma<DT>(read_tr(kt, to.tr_ofs[dt], c), pk[c], acc[dt]);
+            for (int dt = 0; dt < NT; ++dt) acc[dt] = mma<DT>(read_tr<D>(kt, to.tr_ofs[dt], c), pk[c], acc[dt]);
     };
     // One staged 64-key block: tiles A (keys kb..kb+31) and B (kb+32..).  B's
     // products are issued before A's exponentials and A's dQ products before
@@ -267,29 +284,35 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
         f32x16 sA, dA, sB, dB;
         u32x4 pA[2], pB[2];
         prod(kc, vc, sA, dA);
-        if (FA2_BWD_PIPE_Q && doB) prod(kc + 32 * kD, vc + 32 * kD, sB, dB);
+        if (PIPE && doB) prod(kc + 32 * kD, vc + 32 * kD, sB, dB);
+        // D = 128: phase by phase, or the operand reads hoisted across the
+        // phases run out of registers
+        if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
         softgrad(mask_tag, kb, sA, dA, pA);
+        if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
         grad(kc, pA);
         if (doB) {
             // keeps the scheduler from hoisting the second half's operand
             // reads above the first half (which runs out of registers)
             __builtin_amdgcn_sched_barrier(0);
-            if (!FA2_BWD_PIPE_Q) prod(kc + 32 * kD, vc + 32 * kD, sB, dB);
+            if (!PIPE) prod(kc + 32 * kD, vc + 32 * kD, sB, dB);
+            if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
             softgrad(mask_tag, kb + 32, sB, dB, pB);
+            if constexpr (D == 128) __builtin_amdgcn_sched_barrier(0);
             grad(kc + 32 * kD, pB);
         }
     };
 
     if (nblk > 0) {
-        dma_tile(rk, sK, 0, wave, lane);
-        dma_tile(rv, sV, 0, wave, lane);
+        dma_tile<D>(rk, sK, 0, wave, lane);
+        dma_tile<D>(rv, sV, 0, wave, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
     auto block = [&](int b, const uint16_t *kc, const uint16_t *vc, uint16_t *kd, uint16_t *vd) {
         if (b + 1 < nblk) {
-            dma_tile(rk, kd, (b + 1) * kBlk, wave, lane);
-            dma_tile(rv, vd, (b + 1) * kBlk, wave, lane);
+            dma_tile<D>(rk, kd, (b + 1) * kBlk, wave, lane);
+            dma_tile<D>(rv, vd, (b + 1) * kBlk, wave, lane);
         }
         const int kb = b * kBlk;
         // causal: tiles wholly after this wave's last query are skipped
@@ -297,7 +320,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
         const bool doB = !CAUSAL || kb + 32 <= qw + 31;
         const bool mask = kb + kBlk > Nk || (CAUSAL && kb + kBlk - 1 > qw);
         if (doA) {
-            if (mask)
+            // D = 128 always takes the masked path: a second, unmasked copy
+            // of the block does not fit the registers, and the mask's vector
+            // work hides under the twice larger products
+            if (D == 128 || mask)
                 compute(std::true_type{}, kb, kc, vc, doB);
             else
                 compute(std::false_type{}, kb, kc, vc, true);
@@ -313,7 +339,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
     if (qlive) {
         uint16_t *row = dQ + ((size_t)bh * Nq + myq) * kD;
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+        for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int r = 4 * g4;
@@ -328,12 +354,21 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // dK, dV: a workgroup owns 128 keys (32 per wave) of one (b,h) and walks the
 // queries in 64-row tiles (Q, dO, L and D staged in LDS, double-buffered).
-template <int DT, bool CAUSAL>
-__global__ __launch_bounds__(kWaves * 64, CAUSAL ? FA2_BWD_KV_OCC_CAUSAL : FA2_BWD_KV_OCC) void bwd_dkdv_kernel(
+// With D = 128 a workgroup owns 64 keys: waves 2g and 2g + 1 take keys
+// 32g .. 32g + 31, each forms S and D - dP over all 128 columns and keeps
+// the dK, dV accumulators of its own 64 output columns (the full 128 would
+// not fit two waves per SIMD).
+template <int D>
+constexpr int kv_keys_per_wg() { return D == 64 ? 128 : 64; }
+
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(kWaves * 64, D == 128 ? 2 : (CAUSAL ? FA2_BWD_KV_OCC_CAUSAL : FA2_BWD_KV_OCC)) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K, const uint16_t *__restrict__ V,
     const uint16_t *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
     uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int BH, int Nq, int Nk, float scale,
     float scale_log2) {
+    constexpr int kD = D, NC = D / 16;
+    constexpr int KPW = kv_keys_per_wg<D>();
     // two buffers of 64 rows each for Q, dO and (L, D) (tile t in buffer t % 2)
     __shared__ __attribute__((aligned(16))) uint16_t sQ[2 * kBlk * kD];
     __shared__ __attribute__((aligned(16))) uint16_t sG[2 * kBlk * kD];
@@ -344,8 +379,10 @@ __global__ __launch_bounds__(kWaves * 64, CAUSAL ? FA2_BWD_KV_OCC_CAUSAL : FA2_B
     // Workgroup w takes head w % BH and key block w / BH (with causal masking
     // the first key blocks see the most queries, so they start first).
     const int bh = blockIdx.x % BH;
-    const int k0 = (blockIdx.x / BH) * kRows;
-    const int kw = k0 + 32 * wave;  // first key of this wave
+    const int k0 = (blockIdx.x / BH) * KPW;
+    const int kg = D == 64 ? wave : wave >> 1;          // key group of this wave
+    const int dbase = D == 64 ? 0 : 64 * (wave & 1);   // first output column it keeps
+    const int kw = k0 + 32 * kg;  // first key of this wave
     const int myk = kw + ql;
 
     const auto rq = make_rsrc(Q + (size_t)bh * Nq * kD, (uint32_t)Nq * kD * 2);
@@ -358,9 +395,9 @@ __global__ __launch_bounds__(kWaves * 64, CAUSAL ? FA2_BWD_KV_OCC_CAUSAL : FA2_B
     // B operands: chunk dc, slot (h, j) = K[myk][16dc + 8h + j] and -V[..]
     // (sign bits flipped, exact): the dP product then starts from D and
     // yields D - dP, with the sign carried into the final scale of dK.
-    u32x4 kf[4], vf[4];
+    u32x4 kf[NC], vf[NC];
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) {
+    for (int dc = 0; dc < NC; ++dc) {
         kf[dc] = load16(rk, (uint32_t)((myk * kD + 16 * dc + 8 * h) * 2));
         vf[dc] = load16(rv, (uint32_t)((myk * kD + 16 * dc + 8 * h) * 2)) ^ 0x80008000u;
     }
@@ -369,12 +406,12 @@ __global__ __launch_bounds__(kWaves * 64, CAUSAL ? FA2_BWD_KV_OCC_CAUSAL : FA2_B
     // queries this key block sees: causal starts at the tile holding key k0
     const int qstart = CAUSAL ? (k0 / kBlk) * kBlk : 0;
     const int ntile = qstart < Nq ? (Nq - qstart + kBlk - 1) / kBlk : 0;
-    const TileOfs to(lane);
+    const TileOfs<D, 2> to(lane, dbase);
 
     if (Nq % kBlk != 0) {  // rows past Nq are never loaded: keep them finite
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < D / 16; ++i) {
             reinterpret_cast<u32x4 *>(sQ)[tid + 256 * i] = z;
             reinterpret_cast<u32x4 *>(sG)[tid + 256 * i] = z;
         }
@@ -392,7 +429,7 @@ __global__ __launch_bounds__(kWaves * 64, CAUSAL ? FA2_BWD_KV_OCC_CAUSAL : FA2_B
         }
     };
 
-    f32x16 dk[2], dv[2];  // dK^T / dV^T: [dt][r] = X[myk][32dt + 8(r/4) + 4h + r%4]
+    f32x16 dk[2], dv[2];  // dK^T / dV^T: [dt][r] = X[myk][dbase + 32dt + 8(r/4) + 4h + r%4]
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.f;
 
@@ -410,7 +447,7 @@ __global__ __launch_bounds__(kWaves * 64, CAUSAL ? FA2_BWD_KV_OCC_CAUSAL : FA2_B
             for (int i = 0; i < 4; ++i) dn[4 * g4 + i] = d4[i];
         }
 #pragma unroll
-        for (int dc = 0; dc < 4; ++dc) {
+        for (int dc = 0; dc < NC; ++dc) {
             s = mma<DT>(read_row(qt, to.row_ofs[dc]), kf[dc], dc == 0 ? f32x16{} : s);
             dn = mma<DT>(read_row(gt, to.row_ofs[dc]), vf[dc], dn);
         }
@@ -453,8 +490,8 @@ __global__ __launch_bounds__(kWaves * 64, CAUSAL ? FA2_BWD_KV_OCC_CAUSAL : FA2_B
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt) {
-                dv[dt] = mma<DT>(read_tr(gt, to.tr_ofs[dt], c), pp[c], dv[dt]);
-                dk[dt] = mma<DT>(read_tr(qt, to.tr_ofs[dt], c), pd[c], dk[dt]);
+                dv[dt] = mma<DT>(read_tr<D>(gt, to.tr_ofs[dt], c), pp[c], dv[dt]);
+                dk[dt] = mma<DT>(read_tr<D>(qt, to.tr_ofs[dt], c), pd[c], dk[dt]);
             }
     };
     // One staged 64-query tile: sub-tiles A (rows r0..r0+31) and B.  With
@@ -481,8 +518,8 @@ __global__ __launch_bounds__(kWaves * 64, CAUSAL ? FA2_BWD_KV_OCC_CAUSAL : FA2_B
 
     auto stage = [&](int t, uint16_t *qd, uint16_t *gd, float *sld) {
         const int r0 = qstart + t * kBlk;
-        dma_tile(rq, qd, r0, wave, lane);
-        dma_tile(rdo, gd, r0, wave, lane);
+        dma_tile<D>(rq, qd, r0, wave, lane);
+        dma_tile<D>(rdo, gd, r0, wave, lane);
         dma_ld(sld, r0);
     };
     // After wave 0's copy of tile t's L has landed (its own wait), L goes to
@@ -529,7 +566,7 @@ __global__ __launch_bounds__(kWaves * 64, CAUSAL ? FA2_BWD_KV_OCC_CAUSAL : FA2_B
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int r = 4 * g4;
-                const int d = 32 * dt + 8 * g4 + 4 * h;
+                const int d = dbase + 32 * dt + 8 * g4 + 4 * h;
                 u32x2 w;
                 w[0] = pack2<DT>(dk[dt][r] * nscale, dk[dt][r + 1] * nscale);
                 w[1] = pack2<DT>(dk[dt][r + 2] * nscale, dk[dt][r + 3] * nscale);
@@ -541,7 +578,7 @@ __global__ __launch_bounds__(kWaves * 64, CAUSAL ? FA2_BWD_KV_OCC_CAUSAL : FA2_B
     }
 }
 
-template <int DT>
+template <int D, int DT>
 fa2_status bwd_dt(const BwdArgs &a, hipStream_t st) {
     const int bh = a.B * a.H;
     const uint16_t *q = (const uint16_t *)a.q, *k = (const uint16_t *)a.k, *v = (const uint16_t *)a.v;
@@ -549,24 +586,28 @@ fa2_status bwd_dt(const BwdArgs &a, hipStream_t st) {
     const float sl2 = a.scale * kLog2e;
     fa2_status s = FA2_OK;
     if (a.Nq > 0) {
-        s = launch(bwd_delta_kernel<DT>, dim3((a.Nq + 31) / 32, bh), dim3(256), st, o, g, a.delta, a.Nq);
+        constexpr int rows_per_wg = 256 / (D / 8);  // delta kernel: D/8 lanes per row
+        s = launch(bwd_delta_kernel<D, DT>, dim3((a.Nq + rows_per_wg - 1) / rows_per_wg, bh), dim3(256),
+                   st, o, g, a.delta, a.Nq);
         if (s != FA2_OK) return s;
-        auto kq = a.causal ? bwd_dq_kernel<DT, true> : bwd_dq_kernel<DT, false>;
+        auto kq = a.causal ? bwd_dq_kernel<D, DT, true> : bwd_dq_kernel<D, DT, false>;
         s = launch(kq, dim3((unsigned)((a.Nq + kRows - 1) / kRows) * bh), dim3(kWaves * 64), st, q, k, v,
                    g, a.lse, (const float *)a.delta, (uint16_t *)a.dq, bh, a.Nq, a.Nk, a.scale, sl2);
         if (s != FA2_OK) return s;
     }
     // with no queries this still runs: it writes dK = dV = 0
-    auto kk = a.causal ? bwd_dkdv_kernel<DT, true> : bwd_dkdv_kernel<DT, false>;
-    return launch(kk, dim3((unsigned)((a.Nk + kRows - 1) / kRows) * bh), dim3(kWaves * 64), st, q, k,
-                  v, g, a.lse, (const float *)a.delta, (uint16_t *)a.dk, (uint16_t *)a.dv, bh, a.Nq,
-                  a.Nk, a.scale, sl2);
+    constexpr int kpw = kv_keys_per_wg<D>();
+    auto kk = a.causal ? bwd_dkdv_kernel<D, DT, true> : bwd_dkdv_kernel<D, DT, false>;
+    return launch(kk, dim3((unsigned)((a.Nk + kpw - 1) / kpw) * bh), dim3(kWaves * 64), st, q, k, v, g,
+                  a.lse, (const float *)a.delta, (uint16_t *)a.dk, (uint16_t *)a.dv, bh, a.Nq, a.Nk,
+                  a.scale, sl2);
 }
 
 }  // namespace
 
-fa2_status launch_bwd_mfma_d64(const BwdArgs &a, fa2_dtype dt, hipStream_t st) {
-    return dt == FA2_F16 ? bwd_dt<1>(a, st) : bwd_dt<2>(a, st);
+fa2_status launch_bwd_mfma(const BwdArgs &a, fa2_dtype dt, hipStream_t st) {
+    if (a.D == 128) return dt == FA2_F16 ? bwd_dt<128, 1>(a, st) : bwd_dt<128, 2>(a, st);
+    return dt == FA2_F16 ? bwd_dt<64, 1>(a, st) : bwd_dt<64, 2>(a, st);
 }
 
 }  // namespace fa2

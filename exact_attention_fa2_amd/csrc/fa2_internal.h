@@ -38,12 +38,13 @@ struct BwdArgs {
     const float *lse;
     void *dq, *dk, *dv;
     float *delta;
-    int B, H, Nq, Nk;
+    int B, H, Nq, Nk, D;
     float scale;
     int causal;
 };
 
-fa2_status launch_bwd_mfma_d64(const BwdArgs &a, fa2_dtype dt, hipStream_t st);
+// f16/bf16 backward on matrix cores, D = 64 or 128.
+fa2_status launch_bwd_mfma(const BwdArgs &a, fa2_dtype dt, hipStream_t st);
 
 struct DecodeArgs {
     const void *q, *k, *v;

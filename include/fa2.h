@@ -136,9 +136,9 @@ size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int causal, 
  *   accumulation; P and dS are rounded to dtype before the two products
  *   that consume them (as P is in attn_fwd); delta, P and dS are formed in
  *   float32.  With Nq == 0, dk and dv are set to zero.
- *   Supported: D == 64; dtype F16, BF16 (F32 -> FA2_ERR_UNSUPPORTED); any
- *   B, H, Nq >= 0 (B*H == 0 enqueues nothing); Nk >= 1; B*H*ceil(max(Nq,Nk)
- *   / 128) < 2^24.
+ *   Supported: D == 64 or 128; dtype F16, BF16 (F32 -> FA2_ERR_UNSUPPORTED);
+ *   any B, H, Nq >= 0 (B*H == 0 enqueues nothing); Nk >= 1;
+ *   B*H*ceil(max(Nq,Nk) / W) < 2^24 with W = 128 (D = 64) or 64 (D = 128).
  */
 fa2_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
                     const void *dout, const float *lse, void *dq, void *dk, void *dv,

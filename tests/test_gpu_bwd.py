@@ -34,10 +34,10 @@ U = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 FLOOR = 1e-5
 
 
-def run(B, H, Nq, Nk, dt, scale, causal, seed, heads=None):
+def run(B, H, Nq, Nk, dt, scale, causal, seed, heads=None, D=64):
     import torch
-    q, k, v = inputs.qkv((B, H, Nq, 64), (B, H, Nk, 64), seed, dt)
-    g = inputs.normal((B, H, Nq, 64), seed, 3, dt)
+    q, k, v = inputs.qkv((B, H, Nq, D), (B, H, Nk, D), seed, dt)
+    g = inputs.normal((B, H, Nq, D), seed, 3, dt)
     tq, tk, tv, tg = (upload(x, dt) for x in (q, k, v, g))
     if Nq > 0:
         o, lse = fa2.attn_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=True)
@@ -45,14 +45,14 @@ def run(B, H, Nq, Nk, dt, scale, causal, seed, heads=None):
         o, lse = torch.empty_like(tq), torch.empty((B, H, 0), dtype=torch.float32, device="cuda")
     dq, dk, dv, delta = fa2.attn_bwd(tq, tk, tv, o, tg, lse, scale=scale, causal=causal)
     torch.cuda.synchronize()
-    got = [download_f64(t).reshape(B * H, -1, 64) for t in (dq, dk, dv)]
+    got = [download_f64(t).reshape(B * H, -1, D) for t in (dq, dk, dv)]
     got.append(download_f64(delta).reshape(B * H, -1))
     q64, k64, v64, g64 = (inputs.to_f64(x, dt) for x in (q, k, v, g))
     ref = oracle.attn_bwd(q64, k64, v64, g64, scale, causal, heads=heads)
     if heads is not None:
         got = [x[heads] for x in got]
-        g64 = g64.reshape(B * H, Nq, 64)[heads]
-    return got, ref, g64.reshape(len(got[0]), Nq, 64)
+        g64 = g64.reshape(B * H, Nq, D)[heads]
+    return got, ref, g64.reshape(len(got[0]), Nq, D)
 
 
 def check(name, dt, got, ref, g64):
@@ -112,6 +112,34 @@ def test_bwd_bench_shape_heads(dt, causal):
     check(name, dt, got, ref, g64)
 
 
+SMALL_D128 = [  # B, H, Nq, Nk, causal
+    (1, 2, 256, 256, False), (1, 2, 256, 256, True), (1, 1, 300, 200, False),
+    (1, 2, 333, 333, True), (2, 1, 100, 1000, False), (1, 1, 1000, 70, False),
+    (1, 1, 1, 1, False), (1, 1, 1, 1, True), (1, 1, 65, 65, True), (1, 2, 1024, 1024, True),
+]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("B,H,Nq,Nk,causal", SMALL_D128)
+def test_bwd_parity_d128(B, H, Nq, Nk, causal, dt):
+    """Head dimension 128: two waves share each 32 keys of the dK/dV pass and
+    split its output columns; same bounds as D = 64."""
+    scale = 1.0 / 128 ** 0.5
+    name = "bwd D128 B%d H%d Nq%d Nk%d %s %s" % (B, H, Nq, Nk, dt, "causal" if causal else "full")
+    print(name, flush=True)
+    got, ref, g64 = run(B, H, Nq, Nk, dt, scale, causal, seed=8, D=128)
+    check(name, dt, got, ref, g64)
+
+
+@pytest.mark.parametrize("dt,causal", [("f16", False), ("bf16", False), ("f16", True)])
+def test_bwd_d128_bench_shape_heads(dt, causal):
+    heads = [0, 23, 47]
+    name = "bwd B4 H12 N2048 D128 %s %s heads %s" % (dt, "causal" if causal else "full", heads)
+    print(name, flush=True)
+    got, ref, g64 = run(4, 12, 2048, 2048, dt, 1.0 / 128 ** 0.5, causal, seed=0, heads=heads, D=128)
+    check(name, dt, got, ref, g64)
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 def test_bwd_no_queries(dt):
     """Nq = 0: no query attends any key, so dK = dV = 0 exactly."""
@@ -129,7 +157,7 @@ def test_bwd_no_queries(dt):
 
 
 def test_bwd_rejects():
-    """f32 and D != 64 are refused before anything is enqueued."""
+    """f32, and D other than 64 and 128, are refused before anything is enqueued."""
     import torch
     q = torch.zeros(1, 1, 8, 64, device="cuda")
     lse = torch.zeros(1, 1, 8, device="cuda")
