@@ -145,7 +145,8 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
     float *__restrict__ o_part, float *__restrict__ m_part, float *__restrict__ l_part,
-    float *__restrict__ l2_part, int Nq, int Nk, float scale_log2, int n_qtiles, int n_tiles) {
+    float *__restrict__ l2_part, int Nq, int Nk, float scale_log2, int n_qtiles, int n_tiles,
+    int snake) {
     static_assert((D == 64 || D == 128) && (D == 64 || QG == 1), "head dimension");
     constexpr int kD = D;
     constexpr int NC = D / 16;                      // 16-wide contraction chunks of S^T = K Q^T
@@ -171,11 +172,29 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
 
     // Workgroups go round-robin to the 8 XCDs; give each XCD a contiguous run
     // of tiles so the query tiles of one head share that XCD's L2.
-    int wg = blockIdx.x;
-    if ((n_tiles & 7) == 0) wg = (wg & 7) * (n_tiles >> 3) + (wg >> 3);
-    const int bh = wg / n_qtiles;
-    int qt = wg - bh * n_qtiles;
-    if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
+    int bh, qt;
+    if (CAUSAL && snake > 0) {
+        // Causal grid within one round of slots: the p-th workgroup sent to
+        // an XCD lands on its CU p % snake in round p / snake.  Rank the
+        // XCD's tiles by length (longest first) and deal ranks to the CUs in
+        // a snake -- forward in even rounds, backward in odd ones -- so each
+        // CU's tiles add up to about the same number of key blocks (handing
+        // out longest first would give one CU the longest tile of three
+        // heads).  The host checks that heads do not straddle XCDs.
+        const int per_xcd = n_tiles >> 3, hpx = per_xcd / n_qtiles;
+        const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+        const int r = pos / snake, i = pos - r * snake;
+        const int cnt = min(snake, per_xcd - r * snake);  // workgroups in this round
+        const int k = r * snake + ((r & 1) ? cnt - 1 - i : i);
+        qt = n_qtiles - 1 - k / hpx;
+        bh = xcd * hpx + k % hpx;
+    } else {
+        int wg = blockIdx.x;
+        if ((n_tiles & 7) == 0) wg = (wg & 7) * (n_tiles >> 3) + (wg >> 3);
+        bh = wg / n_qtiles;
+        qt = wg - bh * n_qtiles;
+        if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
+    }
     const int q0 = qt * ROWS;
     const int qw = q0 + wave * 32 * QG;  // first row of this wave; group g starts at qw + 32g
 
@@ -531,6 +550,9 @@ struct Plan {
 #ifndef FA2_MFMA_QG2
 #define FA2_MFMA_QG2 1  // 1: 64 query rows per wave when the tiles fill the device twice over; 2: always
 #endif
+#ifndef FA2_MFMA_SNAKE
+#define FA2_MFMA_SNAKE 1  // causal tiles in one round: deal them to CUs in a snake by length
+#endif
 #ifndef FA2_MFMA_SPLIT_LONG
 #define FA2_MFMA_SPLIT_LONG 32  // also split when the tiles fill at most a quarter of the slots
                                 // and the keys span at least this many 64-key blocks (0: never)
@@ -575,6 +597,17 @@ size_t part_bytes(const FwdArgs &a, int chunks) {
     return (size_t)a.B * a.H * a.Nq * chunks * (a.D + 3) * sizeof(float);
 }
 
+// CUs per XCD for the causal snake order (0: keep longest first): only when
+// all tiles fit one round of workgroup slots and every XCD holds whole heads.
+template <int D, int QG>
+int snake_cus(const FwdArgs &a, const Plan &p) {
+    if (!a.causal || FA2_MFMA_SNAKE == 0 || p.n_tiles % 8 != 0 || a.num_cus % 8 != 0) return 0;
+    const int per_xcd = p.n_tiles / 8;
+    const long long slots = (long long)a.num_cus * (QG == 1 && D == 64 ? 3 : 2);
+    if (per_xcd % p.n_qtiles != 0 || p.n_tiles > slots) return 0;
+    return a.num_cus / 8;
+}
+
 template <int D, int DT, bool CAUSAL, bool WLSE, int QG>
 fa2_status launch_q(const FwdArgs &a, const Plan &p, hipStream_t st) {
     const uint16_t *q = (const uint16_t *)a.q, *k = (const uint16_t *)a.k, *v = (const uint16_t *)a.v;
@@ -588,7 +621,7 @@ fa2_status launch_q(const FwdArgs &a, const Plan &p, hipStream_t st) {
         fa2_status s = launch(fwd_mfma_kernel<D, DT, CAUSAL, WLSE, true, QG>,
                               dim3((unsigned)p.n_tiles, (unsigned)p.chunks), dim3(kWaves * 64), st,
                               q, k, v, (uint16_t *)a.o, a.lse, o_part, m_part, l_part, l2_part, a.Nq,
-                              a.Nk, sl2, p.n_qtiles, p.n_tiles);
+                              a.Nk, sl2, p.n_qtiles, p.n_tiles, 0);
         if (s != FA2_OK) return s;
         return launch_combine_rows(o_part, m_part, l_part, a.o, a.lse, (size_t)a.B * a.H * a.Nq, D,
                                    p.chunks, DT == 1 ? FA2_F16 : FA2_BF16, st,
@@ -597,7 +630,7 @@ fa2_status launch_q(const FwdArgs &a, const Plan &p, hipStream_t st) {
     return launch(fwd_mfma_kernel<D, DT, CAUSAL, WLSE, false, QG>, dim3((unsigned)p.n_tiles),
                   dim3(kWaves * 64), st, q, k, v, (uint16_t *)a.o, a.lse, (float *)nullptr,
                   (float *)nullptr, (float *)nullptr, (float *)nullptr, a.Nq, a.Nk, sl2,
-                  p.n_qtiles, p.n_tiles);
+                  p.n_qtiles, p.n_tiles, snake_cus<D, QG>(a, p));
 }
 
 template <int D, int DT, bool CAUSAL, bool WLSE>

@@ -38,6 +38,19 @@ def test_multihead_2048_sampled(dt, causal):
     check_full(cfg, rows)
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_causal_one_round_snake_order(dt):
+    """B2 H12 N2048 causal D128: 384 tiles within one round of slots (two per
+    compute unit at D = 128), dealt to the compute units in a snake."""
+    cfg = workloads.Prefill("B2 H12 N2048 D128 causal %s" % dt, 2, 12, 2048, 2048, D, dt, SCALE,
+                            True, 26)
+    g = np.random.default_rng(5)
+    total = cfg.B * cfg.H * cfg.Nq
+    rows = np.unique(np.concatenate([np.arange(2048), total - 2048 + np.arange(2048),
+                                     g.choice(total, 1024, replace=False)]))
+    check_full(cfg, rows, edge=(dt == "bf16"))
+
+
 RAGGED = [  # (B, H, Nq, Nk, causal)
     (1, 1, 1, 1, False), (1, 1, 1, 1, True), (2, 3, 77, 131, False), (1, 2, 200, 200, True),
     (3, 1, 129, 65, False), (1, 1, 17, 1000, False), (2, 2, 300, 300, True), (1, 1, 64, 1, False),
