@@ -309,31 +309,46 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
-    auto block = [&](int b, const uint16_t *kc, const uint16_t *vc, uint16_t *kd, uint16_t *vd) {
+    // One staged block; MASK selects the masked path (keys past Nk, and
+    // with causal masking keys after this wave's rows, including whole
+    // tiles past its last row).
+    auto block = [&](auto mask_tag, int b, const uint16_t *kc, const uint16_t *vc, uint16_t *kd,
+                     uint16_t *vd) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         if (b + 1 < nblk) {
             dma_tile<D>(rk, kd, (b + 1) * kBlk, wave, lane);
             dma_tile<D>(rv, vd, (b + 1) * kBlk, wave, lane);
         }
         const int kb = b * kBlk;
-        // causal: tiles wholly after this wave's last query are skipped
-        const bool doA = !CAUSAL || kb <= qw + 31;
-        const bool doB = !CAUSAL || kb + 32 <= qw + 31;
-        const bool mask = kb + kBlk > Nk || (CAUSAL && kb + kBlk - 1 > qw);
-        if (doA) {
-            // D = 128 always takes the masked path: a second, unmasked copy
-            // of the block does not fit the registers, and the mask's vector
-            // work hides under the twice larger products
-            if (D == 128 || mask)
-                compute(std::true_type{}, kb, kc, vc, doB);
-            else
-                compute(std::false_type{}, kb, kc, vc, true);
+        if constexpr (MASK) {
+            // causal: tiles wholly after this wave's last query are skipped
+            const bool doA = !CAUSAL || kb <= qw + 31;
+            const bool doB = !CAUSAL || kb + 32 <= qw + 31;
+            if (doA) compute(std::true_type{}, kb, kc, vc, doB);
+        } else {
+            compute(std::false_type{}, kb, kc, vc, true);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
-    for (int b = 0; b < nblk; ++b) {
+    // The blocks that need no mask come first (all keys < Nk and, causal,
+    // <= this wave's first row): they run in a loop of their own, the rest
+    // in a second one, so each loop has one copy of the block and its
+    // accumulators stay in place (one loop with both paths made the compiler
+    // copy them every block).  D = 128 masks every block: a second copy does
+    // not fit its registers, and the mask's vector work hides under the
+    // twice larger products.  Waves may split at different blocks; each
+    // still passes one barrier per block.
+    int bm = D == 128 ? 0 : min(nblk, Nk / kBlk);
+    if (CAUSAL) bm = min(bm, (qw + 1) / kBlk);
+    int b = 0;
+    for (; b < bm; ++b) {
         const int cur = (b & 1) * kBlk * kD, nxt = kBlk * kD - cur;
-        block(b, sK + cur, sV + cur, sK + nxt, sV + nxt);
+        block(std::false_type{}, b, sK + cur, sV + cur, sK + nxt, sV + nxt);
+    }
+    for (; b < nblk; ++b) {
+        const int cur = (b & 1) * kBlk * kD, nxt = kBlk * kD - cur;
+        block(std::true_type{}, b, sK + cur, sV + cur, sK + nxt, sV + nxt);
     }
 
     if (qlive) {
@@ -535,26 +550,37 @@ __global__ __launch_bounds__(kWaves * 64, D == 128 ? 2 : (CAUSAL ? FA2_BWD_KV_OC
         seal(0, sL);
         __syncthreads();
     }
-    auto tile = [&](int t, const uint16_t *qc, const uint16_t *gc, const float *slc, uint16_t *qd,
-                    uint16_t *gd, float *sld) {
+    auto tile = [&](auto mask_tag, int t, const uint16_t *qc, const uint16_t *gc, const float *slc,
+                    uint16_t *qd, uint16_t *gd, float *sld) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         if (t + 1 < ntile) stage(t + 1, qd, gd, sld);
         const int r0 = qstart + t * kBlk;
-        const bool doA = !CAUSAL || r0 + 31 >= kw;
-        const bool doB = !CAUSAL || r0 + 63 >= kw;
-        if (doB) {
-            if (CAUSAL && r0 < kw + 31)  // some query of the tile is before some key
-                compute(std::true_type{}, r0, qc, gc, slc, doA);
-            else
-                compute(std::false_type{}, r0, qc, gc, slc, true);
+        if constexpr (MASK) {  // some query of the tile is before some key (causal)
+            const bool doA = r0 + 31 >= kw;
+            const bool doB = r0 + 63 >= kw;
+            if (doB) compute(std::true_type{}, r0, qc, gc, slc, doA);
+        } else {
+            compute(std::false_type{}, r0, qc, gc, slc, true);
         }
         __builtin_amdgcn_s_waitcnt(0);
         if (t + 1 < ntile) seal(t + 1, sld);
         __syncthreads();
     };
-    for (int t = 0; t < ntile; ++t) {
+    // Causal: the tiles on this wave's diagonal (a query before one of its
+    // keys) come first and take the masked path in a loop of their own; the
+    // rest run unmasked in a second loop (one copy of the tile per loop keeps
+    // the accumulators in place).  Each wave still passes one barrier per tile.
+    const int tm = CAUSAL ? min(ntile, (kw + 31 - qstart + kBlk - 1) / kBlk) : 0;
+    int t = 0;
+    for (; t < tm; ++t) {
         const int cur = (t & 1) * kBlk * kD, nxt = kBlk * kD - cur;
         const int lcur = (t & 1) * 2 * kBlk, lnxt = 2 * kBlk - lcur;
-        tile(t, sQ + cur, sG + cur, sL + lcur, sQ + nxt, sG + nxt, sL + lnxt);
+        tile(std::true_type{}, t, sQ + cur, sG + cur, sL + lcur, sQ + nxt, sG + nxt, sL + lnxt);
+    }
+    for (; t < ntile; ++t) {
+        const int cur = (t & 1) * kBlk * kD, nxt = kBlk * kD - cur;
+        const int lcur = (t & 1) * 2 * kBlk, lnxt = 2 * kBlk - lcur;
+        tile(std::false_type{}, t, sQ + cur, sG + cur, sL + lcur, sQ + nxt, sG + nxt, sL + lnxt);
     }
 
     if (klive) {
