@@ -52,7 +52,7 @@ namespace fa2 {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kRows = 128;  // rows (queries or keys) a workgroup owns: 32 per wave
+constexpr int kRows = 128;  // query rows a dQ workgroup owns (32 per wave); keys of a D = 64 dK/dV one
 constexpr int kBlk = 64;    // rows of the other side staged per block
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
