@@ -205,12 +205,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
     const auto rk = make_rsrc(K + (size_t)bh * Nk * kD, (uint32_t)Nk * kD * 2);
     const auto rv = make_rsrc(V + (size_t)bh * Nk * kD, (uint32_t)Nk * kD * 2);
 
-    // B operands: chunk dc, slot (h, j) = X[myq][16dc + 8h + j]
+    // B operands: chunk dc, slot (h, j) = Q[myq][16dc + 8h + j] and -dO[..]
+    // (sign bits flipped, exact): the dP product then starts from D and
+    // yields D - dP, with the sign carried into the final scale of dQ.
     u32x4 qf[NC], gf[NC];
 #pragma unroll
     for (int dc = 0; dc < NC; ++dc) {
         qf[dc] = load16(rq, (uint32_t)((myq * kD + 16 * dc + 8 * h) * 2));
-        gf[dc] = load16(rdo, (uint32_t)((myq * kD + 16 * dc + 8 * h) * 2));
+        gf[dc] = load16(rdo, (uint32_t)((myq * kD + 16 * dc + 8 * h) * 2)) ^ 0x80008000u;
     }
     const bool qlive = myq < Nq;
     const float l2 = qlive ? LSE[(size_t)bh * Nq + myq] * kLog2e : 0.f;  // base-2 units
@@ -236,18 +238,21 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-    // S^T and dP^T of one 32-key tile (rows kt / vt of the staged block):
-    // s[r], dp[r] belong to key k0 + 8(r/4) + 4h + r%4 and query myq.
-    auto prod = [&](const uint16_t *kt, const uint16_t *vt, f32x16 &s, f32x16 &dp) {
+    // S^T and D - dP^T of one 32-key tile (rows kt / vt of the staged
+    // block): s[r], dn[r] belong to key k0 + 8(r/4) + 4h + r%4 and query myq.
+    auto prod = [&](const uint16_t *kt, const uint16_t *vt, f32x16 &s, f32x16 &dn) {
+        f32x16 d0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) d0[i] = dlt;
 #pragma unroll
         for (int dc = 0; dc < NC; ++dc) {
             s = mma<DT>(read_row(kt, to.row_ofs[dc]), qf[dc], dc == 0 ? f32x16{} : s);
-            dp = mma<DT>(read_row(vt, to.row_ofs[dc]), gf[dc], dc == 0 ? f32x16{} : dp);
+            dn = mma<DT>(read_row(vt, to.row_ofs[dc]), gf[dc], dc == 0 ? d0 : dn);
         }
     };
-    // dS^T = P^T o (dP^T - D), rounded and packed as the B operand of dQ^T.
+    // -dS^T = P^T o (D - dP^T), rounded and packed as the B operand of dQ^T.
     // Keys past Nk and (causal) keys after the query get P = 0 when MASK.
-    auto softgrad = [&](auto mask_tag, int k0, const f32x16 &s, const f32x16 &dp, u32x4 *pk)
+    auto softgrad = [&](auto mask_tag, int k0, const f32x16 &s, const f32x16 &dn, u32x4 *pk)
         __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
                         if (CAUSAL) live = live && key <= myq;
                         x = live ? x : -INFINITY;
                     }
-                    ds2[e] = exp2f_fast(x) * (dp[r] - dlt);
+                    ds2[e] = exp2f_fast(x) * dn[r];
                 }
                 pk[c][j] = pack2<DT>(ds2[0], ds2[1]);
             }
@@ -352,6 +357,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
     }
 
     if (qlive) {
+        const float nscale = -scale;  // the accumulated dS had its sign flipped
         uint16_t *row = dQ + ((size_t)bh * Nq + myq) * kD;
 #pragma unroll
         for (int dt = 0; dt < NT; ++dt)
@@ -359,8 +365,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int r = 4 * g4;
                 u32x2 w;
-                w[0] = pack2<DT>(acc[dt][r] * scale, acc[dt][r + 1] * scale);
-                w[1] = pack2<DT>(acc[dt][r + 2] * scale, acc[dt][r + 3] * scale);
+                w[0] = pack2<DT>(acc[dt][r] * nscale, acc[dt][r + 1] * nscale);
+                w[1] = pack2<DT>(acc[dt][r + 2] * nscale, acc[dt][r + 3] * nscale);
                 *reinterpret_cast<u32x2 *>(row + 32 * dt + 8 * g4 + 4 * h) = w;
             }
     }
