@@ -16,12 +16,15 @@
 //
 // Layouts are those of the forward kernel (32x32x16 MFMA, accumulator lane l
 // register r = row 8(r/4) + 4(l/32) + r%4, column l%32):
-//   dQ kernel:  S^T = K Q^T and dP^T = V dO^T (keys x queries, one query per
-//               lane), dQ^T += K^T dS^T with K^T read by the transposed LDS
-//               load;
-//   dK/dV:      S = Q K^T and dP = dO V^T (queries x keys, one key per lane),
-//               dV^T += dO^T P and dK^T += Q^T dS, dO^T and Q^T transposed
-//               from LDS.
+//   dQ kernel:  S^T = K Q^T and D - dP^T = V (-dO)^T + D (keys x queries,
+//               one query per lane), dQ^T -= K^T (-dS^T) with K^T read by the
+//               transposed LDS load;
+//   dK/dV:      S = Q K^T and D - dP = dO (-V)^T + D (queries x keys, one key
+//               per lane), dV^T += dO^T P and dK^T -= Q^T (-dS), dO^T and Q^T
+//               transposed from LDS.
+// (dO, resp. V, is negated once in registers so that the product starts
+// from D and no per-element subtraction is needed; the sign of dS is undone
+// in the final scale.)
 // Every LDS tile is read both by rows (b128) and transposed (tr_b16); its
 // 16-byte chunks are swizzled so that neither read has bank conflicts.
 #include <type_traits>
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_kernel(
         __syncthreads();
     }
 
-    f32x16 acc[NT];  // dQ^T: acc[dt][r] = dQ[myq][32dt + 8(r/4) + 4h + r%4] / scale
+    f32x16 acc[NT];  // dQ^T: acc[dt][r] = -dQ[myq][32dt + 8(r/4) + 4h + r%4] / scale
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
