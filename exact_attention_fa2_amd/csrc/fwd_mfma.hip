@@ -68,13 +68,15 @@ constexpr float kLazyCap = 256.f;
 
 // Tuning knobs (compile-time).  FA2_KSWZ selects the K-tile chunk swizzle:
 // 1 = chunk ^ ((key/2) % 8), conflict-free for 16 lanes x 16 bytes over 64
-// banks; 0 = chunk ^ (key % 8).  FA2_SGB = 1 pins the issue order inside a tile
-// (score MFMAs interleaved with the exponentials) with scheduling barriers.
+// banks; 0 = chunk ^ (key % 8).  FA2_SGB pins the issue order inside a tile
+// (score MFMAs interleaved with the exponentials) with scheduling barriers:
+// 0 never, 1 always, 2 with D = 128 only (at D = 64 the compiler's own order
+// measured about 1% faster, at D = 128 the pinned one about 0.5%).
 #ifndef FA2_KSWZ
 #define FA2_KSWZ 1
 #endif
 #ifndef FA2_SGB
-#define FA2_SGB 1
+#define FA2_SGB 2
 #endif
 // FA2_VSWZ selects the V-tile swizzle (V is only read transposed, 32 lanes x
 // 8 bytes per pass over 4 consecutive keys): 1 = chunk ^ (j ^ 4(j % 2)) with
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
 #pragma unroll
         for (int g = 0; g < QG; ++g) exps(g, m[g] == -INFINITY ? 0.f : m[g], true);
 #if FA2_SGB
-        if constexpr (NEXT && QG == 1) {
+        if constexpr (NEXT && QG == 1 && (FA2_SGB == 1 || D == 128)) {
 #pragma unroll
             for (int j = 0; j < NC; ++j) {
                 __builtin_amdgcn_sched_group_barrier(0x002, (WLSE ? 32 : 24) / NC, 0);
