@@ -40,6 +40,37 @@ constexpr int kQT = 16;     // query rows per workgroup
 constexpr int kWaves = 16;  // waves per workgroup (4 per SIMD), each on its own key slice
 constexpr int kStep = 16;   // keys per step
 
+#ifndef FA2_F32_ORDER
+#define FA2_F32_ORDER 1  // 1: 1D grid, b*h fastest, causal longest first; 0: (tile, b*h) grid
+#endif
+
+// Query tile and head of this workgroup.  The grid is one-dimensional with
+// b*h varying fastest: consecutive workgroups take the same query tile of
+// different heads, so under a causal mask they have the same length, and the
+// longest tiles go first.  Workgroups reach the XCDs (and, within one, its
+// shader engines) in turn; with the query tile varying fastest instead, each
+// shader engine would get the same few tiles of every head and the one holding
+// the last tiles would carry a full unmasked load.  With b*h a multiple of 8,
+// each XCD also sees only every eighth head, and its L2 holds their K and V.
+template <bool CAUSAL>
+__device__ __forceinline__ void tile_of(int n_qtiles, int &qt, int &bh) {
+    if (FA2_F32_ORDER) {
+        const int n_bh = gridDim.x / n_qtiles;
+        qt = blockIdx.x / n_bh;
+        bh = blockIdx.x - qt * n_bh;
+        if (CAUSAL) qt = n_qtiles - 1 - qt;
+    } else {
+        qt = blockIdx.x;
+        bh = blockIdx.y;
+    }
+}
+
+// Grid of n_qtiles query tiles for each of n_bh heads (chunks key chunks).
+inline dim3 tile_grid(long long n_qtiles, long long n_bh, int chunks) {
+    if (FA2_F32_ORDER) return dim3((unsigned)(n_qtiles * n_bh), 1, (unsigned)chunks);
+    return dim3((unsigned)n_qtiles, (unsigned)n_bh, (unsigned)chunks);
+}
+
 struct KVRegs {
     f32x4 k[4];   // k[j] = K[key k0 + c][16j + 4g .. 16j + 4g + 3]
     f32x4 v[4];   // v[t] = V[key k0 + 4g + t][4c .. 4c+3], t = 0..3
@@ -67,8 +98,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
     // wave index as a wave-uniform value, so the key loop below is scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c = lane & 15;
-    const int q0 = blockIdx.x * kQT;
-    const int bh = blockIdx.y;
+    int qt, bh;
+    tile_of<CAUSAL>((Nq + kQT - 1) / kQT, qt, bh);
+    const int q0 = qt * kQT;
 
     const float *Qh = Q + (size_t)bh * Nq * kD;
     const float *Kh = K + (size_t)bh * Nk * kD;
@@ -142,7 +174,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
         mx = max_xor32(max_xor16(mx));
         const float m_new = fmaxf(m, mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float corr = exp2f_fast(m - m_use);
+        // Rescale only when some row's maximum moved: otherwise the factor
+        // is exactly 1 and the products would change nothing.
+        if (__builtin_amdgcn_ballot_w64(m_new != m) != 0) {
+            const float corr = exp2f_fast(m - m_use);
+            l *= corr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] *= corr;
+        }
         float p[4];
         float psum = 0.f;
 #pragma unroll
@@ -150,9 +189,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
             p[r] = exp2f_fast(s[r] - m_use);
             psum += p[r];
         }
-        l = l * corr + psum;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] *= corr;
+        l += psum;
         // O^T += V^T P^T: slot g pairs key k0 + 4g + t; row m of tile j is d = 4m + j.
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -243,8 +280,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void kernel(
     const int qa = wave & (kTiles - 1);  // query tile of this wave
     const int ss = wave / kTiles;        // key sub-slice of this wave
     const int g = lane >> 4, c = lane & 15;
-    const int q0 = blockIdx.x * kRows;
-    const int bh = blockIdx.y;
+    int qt, bh;
+    tile_of<CAUSAL>((Nq + kRows - 1) / kRows, qt, bh);
+    const int q0 = qt * kRows;
     const int chunk = blockIdx.z, nchunks = gridDim.z;
     const int qt0 = q0 + qa * kQT;  // first row of this wave's tile
 
@@ -478,12 +516,14 @@ size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int num_cus) {
 #endif
 
 fa2_status launch_fwd_f32_d64(const FwdArgs &a, hipStream_t st) {
+    // one-dimensional grids of 16-row tiles (the most numerous) must fit a grid dimension
+    if ((long long)a.B * a.H * ((a.Nq + kQT - 1) / kQT) > 0x7FFFFFFFLL) return FA2_ERR_UNSUPPORTED;
     const float sl2 = a.scale * kLog2e;
     const long long groups = (long long)a.B * a.H * ((a.Nq + shared::kRows - 1) / shared::kRows);
     const dim3 block(kWaves * 64);
     if (FA2_F32_SHARED && groups >= a.num_cus) {
         // enough 64-row groups to fill the device: share K/V, no split
-        const dim3 grid((a.Nq + shared::kRows - 1) / shared::kRows, a.B * a.H, 1);
+        const dim3 grid = tile_grid((a.Nq + shared::kRows - 1) / shared::kRows, a.B * a.H, 1);
         auto k = a.causal ? shared::kernel<true, false> : shared::kernel<false, false>;
         return launch(k, grid, block, st, (const float *)a.q, (const float *)a.k, (const float *)a.v,
                       (float *)a.o, a.lse, (float *)nullptr, (float *)nullptr, (float *)nullptr,
@@ -496,7 +536,7 @@ fa2_status launch_fwd_f32_d64(const FwdArgs &a, hipStream_t st) {
         float *o_part = (float *)a.ws;
         float *m_part = o_part + rows * c * kD;
         float *l_part = m_part + rows * c;
-        const dim3 grid((a.Nq + shared::kRows - 1) / shared::kRows, a.B * a.H, c);
+        const dim3 grid = tile_grid((a.Nq + shared::kRows - 1) / shared::kRows, a.B * a.H, c);
         auto k = a.causal ? shared::kernel<true, true> : shared::kernel<false, true>;
         fa2_status s = launch(k, grid, block, st, (const float *)a.q, (const float *)a.k,
                               (const float *)a.v, (float *)a.o, a.lse, o_part, m_part, l_part, a.Nq,
@@ -505,7 +545,7 @@ fa2_status launch_fwd_f32_d64(const FwdArgs &a, hipStream_t st) {
         return launch_combine_rows(o_part, m_part, l_part, a.o, a.lse, rows, kD, c, FA2_F32, st);
     }
     // few rows and no workspace: 16-row workgroups fill the device instead
-    const dim3 grid((a.Nq + kQT - 1) / kQT, a.B * a.H);
+    const dim3 grid = tile_grid((a.Nq + kQT - 1) / kQT, a.B * a.H, 1);
     if (a.causal)
         return launch(fwd_f32_d64_kernel<true>, grid, block, st, (const float *)a.q,
                       (const float *)a.k, (const float *)a.v, (float *)a.o, a.lse, a.Nq, a.Nk, sl2);

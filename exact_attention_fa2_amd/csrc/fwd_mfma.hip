@@ -78,6 +78,9 @@ constexpr float kLazyCap = 256.f;
 #ifndef FA2_SGB
 #define FA2_SGB 2
 #endif
+#ifndef FA2_MFMA_ORDER
+#define FA2_MFMA_ORDER 1  // causal, beyond one round of slots: b*h fastest, longest first
+#endif
 // FA2_VSWZ selects the V-tile swizzle (V is only read transposed, 32 lanes x
 // 8 bytes per pass over 4 consecutive keys): 1 = chunk ^ (j ^ 4(j % 2)) with
 // j = (key/2) % 8, under which keys k and k + 2 differ in bit 2 and the read
@@ -190,6 +193,15 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
         const int k = r * snake + ((r & 1) ? cnt - 1 - i : i);
         qt = n_qtiles - 1 - k / hpx;
         bh = xcd * hpx + k % hpx;
+    } else if (CAUSAL && FA2_MFMA_ORDER) {
+        // b*h varies fastest and the longest tiles go first: workgroups that
+        // arrive together have the same length, so the XCDs, and the shader
+        // engines within each, all get the same mix of lengths.  With b*h a
+        // multiple of 8, each XCD sees only every eighth head.
+        const int n_bh = n_tiles / n_qtiles;
+        const int rank = (int)blockIdx.x / n_bh;
+        qt = n_qtiles - 1 - rank;
+        bh = (int)blockIdx.x - rank * n_bh;
     } else {
         int wg = blockIdx.x;
         if ((n_tiles & 7) == 0) wg = (wg & 7) * (n_tiles >> 3) + (wg >> 3);

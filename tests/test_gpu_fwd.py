@@ -222,7 +222,7 @@ def test_deterministic(dt):
 
 
 F32_SHAPES = [(1, 1, 4096, 4096), (1, 2, 1024, 1024), (1, 1, 200, 200), (2, 3, 77, 131),
-              (8, 48, 256, 256)]
+              (8, 48, 256, 256), (2, 12, 1024, 1024)]
 
 
 @pytest.mark.parametrize("shape,causal",
@@ -233,7 +233,8 @@ def test_f32_schedules(shape, causal):
     """The three float32 schedules, each against the oracle: keys split across
     workgroups with a workspace and the combine, the same call without a
     workspace (16-row workgroups), and many 64-row groups (shared K/V, no
-    split -- the last shape)."""
+    split -- the last two shapes, the second with 16 query tiles per head in
+    two rounds of workgroups)."""
     import torch
     B, H, Nq, Nk = shape
     q, k, v = seeded(B, H, Nq, Nk, 64, "f32", 12)
