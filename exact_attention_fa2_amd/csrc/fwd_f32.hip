@@ -40,10 +40,6 @@ constexpr int kQT = 16;     // query rows per workgroup
 constexpr int kWaves = 16;  // waves per workgroup (4 per SIMD), each on its own key slice
 constexpr int kStep = 16;   // keys per step
 
-#ifndef FA2_F32_ORDER
-#define FA2_F32_ORDER 1  // 1: 1D grid, b*h fastest, causal longest first; 0: (tile, b*h) grid
-#endif
-
 // Query tile and head of this workgroup.  The grid is one-dimensional with
 // b*h varying fastest: consecutive workgroups take the same query tile of
 // different heads, so under a causal mask they have the same length, and the
@@ -54,21 +50,15 @@ constexpr int kStep = 16;   // keys per step
 // each XCD also sees only every eighth head, and its L2 holds their K and V.
 template <bool CAUSAL>
 __device__ __forceinline__ void tile_of(int n_qtiles, int &qt, int &bh) {
-    if (FA2_F32_ORDER) {
-        const int n_bh = gridDim.x / n_qtiles;
-        qt = blockIdx.x / n_bh;
-        bh = blockIdx.x - qt * n_bh;
-        if (CAUSAL) qt = n_qtiles - 1 - qt;
-    } else {
-        qt = blockIdx.x;
-        bh = blockIdx.y;
-    }
+    const int n_bh = gridDim.x / n_qtiles;
+    qt = blockIdx.x / n_bh;
+    bh = blockIdx.x - qt * n_bh;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;
 }
 
 // Grid of n_qtiles query tiles for each of n_bh heads (chunks key chunks).
 inline dim3 tile_grid(long long n_qtiles, long long n_bh, int chunks) {
-    if (FA2_F32_ORDER) return dim3((unsigned)(n_qtiles * n_bh), 1, (unsigned)chunks);
-    return dim3((unsigned)n_qtiles, (unsigned)n_bh, (unsigned)chunks);
+    return dim3((unsigned)(n_qtiles * n_bh), 1, (unsigned)chunks);
 }
 
 struct KVRegs {

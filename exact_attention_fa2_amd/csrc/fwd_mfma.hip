@@ -78,9 +78,6 @@ constexpr float kLazyCap = 256.f;
 #ifndef FA2_SGB
 #define FA2_SGB 2
 #endif
-#ifndef FA2_MFMA_ORDER
-#define FA2_MFMA_ORDER 1  // causal, beyond one round of slots: b*h fastest, longest first
-#endif
 // FA2_VSWZ selects the V-tile swizzle (V is only read transposed, 32 lanes x
 // 8 bytes per pass over 4 consecutive keys): 1 = chunk ^ (j ^ 4(j % 2)) with
 // j = (key/2) % 8, under which keys k and k + 2 differ in bit 2 and the read
@@ -175,8 +172,8 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
     const int h = lane >> 5;
     const int ql = lane & 31;
 
-    // Workgroups go round-robin to the 8 XCDs; give each XCD a contiguous run
-    // of tiles so the query tiles of one head share that XCD's L2.
+    // Workgroups go round-robin to the 8 XCDs (and, within one, to its shader
+    // engines).
     int bh, qt;
     if (CAUSAL && snake > 0) {
         // Causal grid within one round of slots: the p-th workgroup sent to
@@ -193,7 +190,7 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
         const int k = r * snake + ((r & 1) ? cnt - 1 - i : i);
         qt = n_qtiles - 1 - k / hpx;
         bh = xcd * hpx + k % hpx;
-    } else if (CAUSAL && FA2_MFMA_ORDER) {
+    } else if (CAUSAL) {
         // b*h varies fastest and the longest tiles go first: workgroups that
         // arrive together have the same length, so the XCDs, and the shader
         // engines within each, all get the same mix of lengths.  With b*h a
@@ -203,11 +200,12 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
         qt = n_qtiles - 1 - rank;
         bh = (int)blockIdx.x - rank * n_bh;
     } else {
+        // Unmasked tiles all have the same length: give each XCD a contiguous
+        // run of tiles so the query tiles of one head share that XCD's L2.
         int wg = blockIdx.x;
         if ((n_tiles & 7) == 0) wg = (wg & 7) * (n_tiles >> 3) + (wg >> 3);
         bh = wg / n_qtiles;
         qt = wg - bh * n_qtiles;
-        if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
     }
     const int q0 = qt * ROWS;
     const int qw = q0 + wave * 32 * QG;  // first row of this wave; group g starts at qw + 32g
