@@ -222,7 +222,7 @@ def test_deterministic(dt):
 
 
 F32_SHAPES = [(1, 1, 4096, 4096), (1, 2, 1024, 1024), (1, 1, 200, 200), (2, 3, 77, 131),
-              (8, 48, 256, 256), (2, 12, 1024, 1024)]
+              (8, 48, 256, 256), (2, 12, 1024, 1024), (3, 7, 832, 832)]
 
 
 @pytest.mark.parametrize("shape,causal",
@@ -233,8 +233,8 @@ def test_f32_schedules(shape, causal):
     """The three float32 schedules, each against the oracle: keys split across
     workgroups with a workspace and the combine, the same call without a
     workspace (16-row workgroups), and many 64-row groups (shared K/V, no
-    split -- the last two shapes, the second with 16 query tiles per head in
-    two rounds of workgroups)."""
+    split -- the last three shapes: 16 query tiles per head in two rounds of
+    workgroups, then 13 tiles for each of 21 heads, b*h not a multiple of 8)."""
     import torch
     B, H, Nq, Nk = shape
     q, k, v = seeded(B, H, Nq, Nk, 64, "f32", 12)
