@@ -87,9 +87,30 @@ def _check(fn, status):
         raise FA2Error(fn, status)
 
 
-def _contig(t, name):
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
+def _validate(ref, specs):
+    """Every tensor the library reads or writes through a raw pointer: the
+    exact shape and dtype, contiguous, and on the same GPU as ``ref`` (the
+    library cannot see buffer sizes, so a short buffer would be overrun).
+    ``specs`` holds (tensor, name, shape, dtype); shape None checks only the
+    rest (a byte workspace)."""
+    for t, name, shape, dtype in specs:
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError("%s must have shape %s, not %s" % (name, tuple(shape), tuple(t.shape)))
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError("%s must be %s, not %s" % (name, dtype, t.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if ref.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU, not %s" % ref.device)
+    for t, name, _, _ in specs:
+        if t.device != ref.device:
+            raise ValueError("%s must be on %s, not %s" % (name, ref.device, t.device))
+
+
+def _dims(t, n, name):
+    if t.dim() != n:
+        raise ValueError("%s must have %d dimensions, not %d" % (name, n, t.dim()))
+    return tuple(t.shape)
 
 
 def workspace_size(B, H, Nq, Nk, D, causal, dtype_code_) -> int:
@@ -106,21 +127,21 @@ def attn_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=
     ``use_workspace=False`` calls the plain attn_fwd entry point instead.
     Returns o (and lse [B,H,Nq] float32 when ``return_lse``)."""
     torch = _torch()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _contig(t, name)
-    B, H, Nq, D = q.shape
-    Nk = k.shape[2]
-    if k.shape != (B, H, Nk, D) or v.shape != (B, H, Nk, D):
-        raise ValueError("k and v must be [B,H,Nk,D] matching q")
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k and v must share a dtype")
+    B, H, Nq, D = _dims(q, 4, "q")
+    Nk = _dims(k, 4, "k")[2]
+    _validate(q, [(q, "q", (B, H, Nq, D), q.dtype), (k, "k", (B, H, Nk, D), q.dtype),
+                  (v, "v", (B, H, Nk, D), q.dtype)])
+    dc = dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    dc = dtype_code(q)
+    outs = [(out, "out", (B, H, Nq, D), q.dtype)]
+    if return_lse:
+        outs.append((lse, "lse", (B, H, Nq), torch.float32))
+    _validate(q, outs)
     if not use_workspace:
         st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
                             _ptr(lse if return_lse else None), B, H, Nq, Nk, D, float(scale),
@@ -128,6 +149,8 @@ def attn_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=
         _check("attn_fwd", st)
         return (out, lse) if return_lse else out
     need = workspace_size(B, H, Nq, Nk, D, causal, dc)
+    if need and workspace is not None:
+        _validate(q, [(workspace, "workspace", None, None)])
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace) if need else None
@@ -145,28 +168,25 @@ def attn_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, 
     dtype), lse [B,H,Nq] float32 from attn_fwd.  Returns (dq, dk, dv, delta)
     with delta [B,H,Nq] float32 = rowsum(dout * o)."""
     torch = _torch()
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)):
-        _contig(t, name)
-    B, H, Nq, D = q.shape
-    Nk = k.shape[2]
-    if k.shape != (B, H, Nk, D) or v.shape != (B, H, Nk, D):
-        raise ValueError("k and v must be [B,H,Nk,D] matching q")
-    if o.shape != q.shape or dout.shape != q.shape:
-        raise ValueError("o and dout must have q's shape")
-    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
-        raise ValueError("lse must be float32 [B,H,Nq]")
-    if any(t.dtype != q.dtype for t in (k, v, o, dout)):
-        raise TypeError("q, k, v, o and dout must share a dtype")
+    B, H, Nq, D = _dims(q, 4, "q")
+    Nk = _dims(k, 4, "k")[2]
+    qs, ks, f32 = (B, H, Nq, D), (B, H, Nk, D), torch.float32
+    _validate(q, [(q, "q", qs, q.dtype), (k, "k", ks, q.dtype), (v, "v", ks, q.dtype),
+                  (o, "o", qs, q.dtype), (dout, "dout", qs, q.dtype),
+                  (lse, "lse", (B, H, Nq), f32)])
+    dc = dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     if delta is None:
-        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+        delta = torch.empty((B, H, Nq), dtype=f32, device=q.device)
+    _validate(q, [(dq, "dq", qs, q.dtype), (dk, "dk", ks, q.dtype), (dv, "dv", ks, q.dtype),
+                  (delta, "delta", (B, H, Nq), f32)])
     st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                         _ptr(dk), _ptr(dv), _ptr(delta), B, H, Nq, Nk, D, float(scale),
-                        int(bool(causal)), dtype_code(q), _stream(stream))
+                        int(bool(causal)), dc, _stream(stream))
     _check("attn_bwd", st)
     return dq, dk, dv, delta
 
@@ -175,21 +195,27 @@ def attn_decode_split(q, k, v, scale, n_splits, o_part=None, m_part=None, l_part
                       stream=None):
     """Flash-decoding partials.  q [B,H,D], k/v [B,H,N,D]."""
     torch = _torch()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _contig(t, name)
-    B, H, D = q.shape
-    N = k.shape[2]
-    if k.shape != (B, H, N, D) or v.shape != (B, H, N, D):
-        raise ValueError("k and v must be [B,H,N,D] matching q")
+    B, H, D = _dims(q, 3, "q")
+    N = _dims(k, 4, "k")[2]
+    n_splits = int(n_splits)
+    if n_splits < 1:
+        raise ValueError("n_splits must be at least 1")
+    _validate(q, [(q, "q", (B, H, D), q.dtype), (k, "k", (B, H, N, D), q.dtype),
+                  (v, "v", (B, H, N, D), q.dtype)])
+    dc = dtype_code(q)
     if o_part is None:
         o_part = torch.empty((B, H, n_splits, D), dtype=torch.float32, device=q.device)
     if m_part is None:
         m_part = torch.empty((B, H, n_splits), dtype=torch.float32, device=q.device)
     if l_part is None:
         l_part = torch.empty((B, H, n_splits), dtype=torch.float32, device=q.device)
+    f32 = torch.float32
+    _validate(q, [(o_part, "o_part", (B, H, n_splits, D), f32),
+                  (m_part, "m_part", (B, H, n_splits), f32),
+                  (l_part, "l_part", (B, H, n_splits), f32)])
     st = lib().attn_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(m_part),
-                                 _ptr(l_part), B, H, N, D, float(scale), int(n_splits),
-                                 dtype_code(q), _stream(stream))
+                                 _ptr(l_part), B, H, N, D, float(scale), n_splits, dc,
+                                 _stream(stream))
     _check("attn_decode_split", st)
     return o_part, m_part, l_part
 
@@ -197,9 +223,13 @@ def attn_decode_split(q, k, v, scale, n_splits, o_part=None, m_part=None, l_part
 def attn_decode_combine(o_part, m_part, l_part, dtype, out=None, stream=None):
     """Merge partials into o [B,H,D] of ``dtype``."""
     torch = _torch()
-    B, H, S, D = o_part.shape
+    B, H, S, D = _dims(o_part, 4, "o_part")
+    f32 = torch.float32
+    _validate(o_part, [(o_part, "o_part", (B, H, S, D), f32), (m_part, "m_part", (B, H, S), f32),
+                       (l_part, "l_part", (B, H, S), f32)])
     if out is None:
         out = torch.empty((B, H, D), dtype=dtype, device=o_part.device)
+    _validate(o_part, [(out, "out", (B, H, D), dtype)])
     st = lib().attn_decode_combine(_ptr(o_part), _ptr(m_part), _ptr(l_part), _ptr(out), B, H,
                                    D, S, dtype_code(out), _stream(stream))
     _check("attn_decode_combine", st)
@@ -212,8 +242,8 @@ def default_splits(B, H, N, D) -> int:
 
 def attn_decode(q, k, v, scale=None, n_splits=None, stream=None):
     """Split + combine.  q [B,H,D], k/v [B,H,N,D]; returns o [B,H,D]."""
-    B, H, D = q.shape
-    N = k.shape[2]
+    B, H, D = _dims(q, 3, "q")
+    N = _dims(k, 4, "k")[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if n_splits is None:
