@@ -5,8 +5,11 @@
 // Method: the FlashAttention-2 forward ("Flash Attention" (aarnphm.xyz),
 // sections Deriving the online softmax and FlashAttention 2; "06: Fused
 // attention", attn_fwd).  A workgroup owns 128 query rows, one 32-row slab per
-// wave (each wave owns whole rows, so no cross-wave reduction is needed), and
-// walks the keys in blocks of 64 staged through LDS.  Per block and wave:
+// wave (each wave owns whole rows, so no cross-wave reduction is needed), or
+// 256 rows with two slabs per wave (QG = 2, half the LDS reads per flop) when
+// the tiles fill the device in whole rounds, and walks the keys in blocks of
+// 64 staged through LDS; with few tiles the keys are also cut into chunks
+// whose partial states the combine kernel merges.  Per block and wave:
 //     S^T = K Q^T                    (D/8 MFMAs, f32 accumulate)
 //     m_new = max(m, rowmax S);  P = exp(S - m);  l = l*corr + rowsum P
 //     O^T = corr*O^T + V^T P^T       (D/8 MFMAs, P rounded to the input dtype)
