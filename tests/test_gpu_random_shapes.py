@@ -1,0 +1,86 @@
+"""Parity on a fixed list of pseudo-random shapes, forward and backward,
+against the fp64 oracle through the C ABI.
+
+The named workloads and the hand-picked ragged cases test what was designed
+for; this list (drawn once from a seeded generator, so every run checks the
+same cases) mixes batch, heads, lengths from 1 to 2000 (700 backward), head
+dimension, dtype, scale and the causal flag in combinations nobody chose,
+which reach the schedules (key split or not, 128 or 256 rows per workgroup,
+one round of workgroups or several) and their ragged edges in other ways.
+Bounds are those of the other parity tests: gpu_util.edge_tol on O, 1e-4 on
+the LSE, and the backward's u-relative bounds.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from exact_attention_fa2_amd import workloads
+from test_gpu_bwd import check as check_bwd
+from test_gpu_bwd import run as run_bwd
+from test_gpu_fwd import check_full
+
+pytestmark = pytest.mark.gpu
+
+
+def _length(g, hi):
+    """Half log-uniform on [1, hi] (short and ragged), half uniform on
+    [128, hi] (several tiles and blocks)."""
+    if g.integers(2):
+        return int(g.integers(128, hi + 1))
+    return int(min(hi, max(1, round(math.exp(g.uniform(0.0, math.log(hi)))))))
+
+
+def _forward_cases(n=96, seed=2024):
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = ("f32", "f16", "bf16")[i % 3]
+        D = 64 if dt == "f32" else int(g.choice([64, 128]))
+        causal = bool(g.integers(2))
+        B, H = int(g.integers(1, 4)), int(g.integers(1, 5))
+        Nq = _length(g, 2000)
+        Nk = Nq if causal else _length(g, 2000)
+        # scale 0.5 makes the softmax peaky; it is the fused-attention
+        # tutorial's setting at D = 64 only (at D = 128 the f16 bound would not
+        # hold for the largest outputs), so larger D takes 1/sqrt(D)
+        scale = float(g.choice([D ** -0.5, 0.07] + ([0.5] if D == 64 else [])))
+        out.append((B, H, Nq, Nk, D, dt, scale, causal, 1000 + i))
+    return out
+
+
+def _backward_cases(n=32, seed=77):
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = ("f16", "bf16")[i % 2]
+        D = int(g.choice([64, 128]))
+        causal = bool(g.integers(2))
+        B, H = int(g.integers(1, 3)), int(g.integers(1, 4))
+        Nq = _length(g, 700)
+        Nk = Nq if causal else _length(g, 700)
+        out.append((B, H, Nq, Nk, D, dt, D ** -0.5, causal, 2000 + i))
+    return out
+
+
+FWD = _forward_cases()
+BWD = _backward_cases()
+
+
+def _id(c):
+    B, H, Nq, Nk, D, dt, scale, causal, _ = c
+    return "B%dH%d_%dx%d_D%d_%s_s%.3g%s" % (B, H, Nq, Nk, D, dt, scale, "_c" if causal else "")
+
+
+@pytest.mark.parametrize("case", FWD, ids=_id)
+def test_forward(case):
+    B, H, Nq, Nk, D, dt, scale, causal, seed = case
+    check_full(workloads.Prefill("random " + _id(case), B, H, Nq, Nk, D, dt, scale, causal, seed),
+               edge=True)
+
+
+@pytest.mark.parametrize("case", BWD, ids=_id)
+def test_backward(case):
+    B, H, Nq, Nk, D, dt, scale, causal, seed = case
+    got, ref, g64 = run_bwd(B, H, Nq, Nk, dt, scale, causal, seed, D=D)
+    check_bwd("random " + _id(case), dt, got, ref, g64)
