@@ -63,8 +63,41 @@ def _backward_cases(n=32, seed=77):
     return out
 
 
+def _large_forward_cases(n=30, seed=7):
+    """Many heads and long rows: several rounds of workgroups, 256-row tiles,
+    the XCD remap.  Checked on sampled rows."""
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = ("f32", "f16", "bf16")[i % 3]
+        D = 64 if dt == "f32" else int(g.choice([64, 128]))
+        causal = bool(g.integers(2))
+        B, H = int(g.integers(1, 9)), int(g.integers(1, 33))
+        Nq = int(g.integers(128, 4097))
+        Nk = Nq if causal else int(g.integers(128, 4097))
+        out.append((B, H, Nq, Nk, D, dt, float(g.choice([D ** -0.5, 0.07])), causal, 5000 + i))
+    return out
+
+
+def _large_backward_cases(n=12, seed=11):
+    """Up to 64 heads and 2048 rows; checked on a few sampled heads."""
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = ("f16", "bf16")[i % 2]
+        D = int(g.choice([64, 128]))
+        causal = bool(g.integers(2))
+        B, H = int(g.integers(1, 5)), int(g.integers(1, 17))
+        Nq = int(g.integers(64, 2049))
+        Nk = Nq if causal else int(g.integers(64, 2049))
+        out.append((B, H, Nq, Nk, D, dt, D ** -0.5, causal, 7000 + i))
+    return out
+
+
 FWD = _forward_cases()
 BWD = _backward_cases()
+FWD_LARGE = _large_forward_cases()
+BWD_LARGE = _large_backward_cases()
 
 
 def _id(c):
@@ -83,4 +116,24 @@ def test_forward(case):
 def test_backward(case):
     B, H, Nq, Nk, D, dt, scale, causal, seed = case
     got, ref, g64 = run_bwd(B, H, Nq, Nk, dt, scale, causal, seed, D=D)
+    check_bwd("random " + _id(case), dt, got, ref, g64)
+
+
+@pytest.mark.parametrize("case", FWD_LARGE, ids=_id)
+def test_forward_large(case):
+    B, H, Nq, Nk, D, dt, scale, causal, seed = case
+    total = B * H * Nq
+    g = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([g.choice(total, min(total, 384), replace=False),
+                                     np.arange(64), total - 1 - np.arange(64)]))
+    check_full(workloads.Prefill("random " + _id(case), B, H, Nq, Nk, D, dt, scale, causal, seed),
+               rows, edge=True)
+
+
+@pytest.mark.parametrize("case", BWD_LARGE, ids=_id)
+def test_backward_large(case):
+    B, H, Nq, Nk, D, dt, scale, causal, seed = case
+    g = np.random.default_rng(seed)
+    heads = sorted(set(g.choice(B * H, min(B * H, 3), replace=False).tolist()) | {0, B * H - 1})
+    got, ref, g64 = run_bwd(B, H, Nq, Nk, dt, scale, causal, seed, heads=heads, D=D)
     check_bwd("random " + _id(case), dt, got, ref, g64)
