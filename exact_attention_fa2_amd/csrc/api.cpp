@@ -3,6 +3,7 @@
 // frees or synchronises; every launch goes on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -53,6 +54,7 @@ fa2_status fwd_impl(const void *q, const void *k, const void *v, void *o, float 
     if (B < 0 || H < 0 || Nq < 0 || Nk < 1 || D < 1) return FA2_ERR_SHAPE;
     if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
     if (causal != 0 && causal != 1) return FA2_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return FA2_ERR_UNSUPPORTED;
     if (D != 64 && !(D == 128 && dtype != FA2_F32)) return FA2_ERR_UNSUPPORTED;
     if (causal && Nq != Nk) return FA2_ERR_UNSUPPORTED;
     if ((long long)B * H * Nq == 0) return FA2_OK;  // nothing to compute
@@ -108,6 +110,7 @@ FA2_API fa2_status attn_bwd(const void *q, const void *k, const void *v, const v
     if (B < 0 || H < 0 || Nq < 0 || Nk < 1 || D < 1) return FA2_ERR_SHAPE;
     if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
     if (causal != 0 && causal != 1) return FA2_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return FA2_ERR_UNSUPPORTED;
     if ((D != 64 && D != 128) || dtype == FA2_F32) return FA2_ERR_UNSUPPORTED;
     if (causal && Nq != Nk) return FA2_ERR_UNSUPPORTED;
     if ((long long)B * H == 0) return FA2_OK;
@@ -136,6 +139,7 @@ FA2_API fa2_status attn_decode_split(const void *q, const void *k, const void *v
                                      void *stream) {
     if (B < 0 || H < 0 || N < 1 || D < 1 || n_splits < 1) return FA2_ERR_SHAPE;
     if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return FA2_ERR_UNSUPPORTED;
     if (D != 64 && D != 128) return FA2_ERR_UNSUPPORTED;
     if ((long long)B * H == 0) return FA2_OK;
     if (!q || !k || !v || !o_part || !m_part || !l_part) return FA2_ERR_NULL;

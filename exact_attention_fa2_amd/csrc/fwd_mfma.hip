@@ -220,6 +220,16 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
     const auto rk = make_rsrc(Kh, (uint32_t)Nk * kD * 2);
     const auto rv = make_rsrc(Vh, (uint32_t)Nk * kD * 2);
 
+    // The loop below takes row maxima of the unscaled scores and masks keys
+    // with -inf before the scale is applied, which holds for a positive scale
+    // only.  A negative scale is moved onto Q (an exact sign flip) and a zero
+    // scale becomes Q = 0 with scale 1: the scaled scores are the same.  (Q is
+    // changed after the prologue's wait for its loads, so that its latency
+    // still overlaps the first K/V copies.)
+    const uint32_t qflip = scale_log2 < 0.f ? 0x80008000u : 0u;
+    const uint32_t qkeep = scale_log2 == 0.f ? 0u : 0xFFFFFFFFu;
+    scale_log2 = scale_log2 == 0.f ? 1.f : fabsf(scale_log2);
+
     // B operand of S^T = K Q^T for group g: chunk dc, slot (h, j) is
     // Q[qw + 32g + ql][16dc + 8h + j].
     u32x4 qf[QG][NC];
@@ -462,6 +472,10 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
         dma(rk, sK1, b0 * kBC - 32, true);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+#pragma unroll
+        for (int g = 0; g < QG; ++g)
+#pragma unroll
+            for (int dc = 0; dc < NC; ++dc) qf[g][dc] = (qf[g][dc] ^ qflip) & qkeep;
         f32x16 sa[QG], sb[QG];
 #pragma unroll
         for (int dc = 0; dc < NC; ++dc) {

@@ -67,7 +67,10 @@ typedef enum {
  *   lse  [B,H,Nq] float32, natural log of the scaled scores; may be NULL.
  *   causal  0: every key is live.  1: key j is live for query i only when
  *           j <= i (top-left aligned); requires Nq == Nk.
- *   scale   multiplies q.k before the softmax (for example 1/sqrt(D)).
+ *   scale   multiplies q.k before the softmax (for example 1/sqrt(D)); any
+ *           finite value (0 gives equal weights over the live keys, a
+ *           negative scale favours the least similar keys); a NaN or
+ *           infinite scale returns FA2_ERR_UNSUPPORTED.
  *   Arithmetic: float32 softmax state and accumulation.  f16/bf16 inputs run
  *   both products on MFMA with P rounded to the input dtype; float32 inputs
  *   run both products on float32 MFMA (no reduced-precision rounding).
@@ -161,7 +164,8 @@ fa2_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
  *   q [B,H,D] dtype;  k, v [B,H,N,D] dtype
  *   o_part [B,H,n_splits,D] float32;  m_part, l_part [B,H,n_splits] float32
  *   Supported: D in {64, 128}; dtype F16, BF16, F32; N >= 1; n_splits >= 1;
- *   B*H == 0 enqueues nothing.
+ *   any finite scale (otherwise FA2_ERR_UNSUPPORTED); B*H == 0 enqueues
+ *   nothing.
  */
 fa2_status attn_decode_split(const void *q, const void *k, const void *v,
                              float *o_part, float *m_part, float *l_part,

@@ -58,6 +58,8 @@ def test_fwd_error_paths():
     assert _fwd(dt=7) == 3
     assert _fwd(causal=1, Nq=4, Nk=8) == 3
     assert _fwd(causal=2) == 3
+    assert _fwd(scale=float("nan")) == 3
+    assert _fwd(scale=float("inf")) == 3
     assert _fwd(q=None) == 1
     assert _fwd(v=None) == 1
     L = fa2.lib()
@@ -89,6 +91,7 @@ def test_decode_error_paths():
     assert split(ns=0) == 2
     assert split(D=96) == 3
     assert split(dt=5) == 3
+    assert L.attn_decode_split(ok, ok, ok, ok, ok, ok, 1, 1, 64, 128, float("nan"), 4, 1, None) == 3
     assert split(q=None) == 1
     assert split(q=ctypes.c_void_p(4100)) == 4
     assert split(B=0) == 0
@@ -152,6 +155,8 @@ def test_bwd_error_paths():
     assert _bwd(dt=9) == 3
     assert _bwd(causal=1, Nq=4, Nk=8) == 3
     assert _bwd(causal=3) == 3
+    ok = ctypes.c_void_p(4096)
+    assert fa2.lib().attn_bwd(*([ok] * 10), 1, 1, 4, 4, 64, float("-inf"), 0, 1, None) == 3
     for name in ("q", "k", "v", "o", "g", "lse", "dq", "dk", "dv", "delta"):
         assert _bwd(**{name: None}) == 1, name
     # with no queries only k, v, dk and dv are needed

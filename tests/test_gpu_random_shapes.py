@@ -137,3 +137,22 @@ def test_backward_large(case):
     heads = sorted(set(g.choice(B * H, min(B * H, 3), replace=False).tolist()) | {0, B * H - 1})
     got, ref, g64 = run_bwd(B, H, Nq, Nk, dt, scale, causal, seed, heads=heads, D=D)
     check_bwd("random " + _id(case), dt, got, ref, g64)
+
+
+@pytest.mark.parametrize("dt,D", [("f32", 64), ("f16", 64), ("bf16", 64), ("f16", 128),
+                                  ("bf16", 128)])
+@pytest.mark.parametrize("scale", [0.0, -0.125, 2.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_unusual_scales(scale, causal, dt, D):
+    """scale 0 (every score 0: the mean of the live values), a negative scale
+    (attention to the least similar keys) and a large one (one key per row
+    dominates)."""
+    check_full(workloads.Prefill("scale %g" % scale, 2, 3, 200, 200, D, dt, scale, causal, 31),
+               edge=True)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [0.0, -0.125])
+def test_backward_unusual_scales(scale, dt):
+    got, ref, g64 = run_bwd(1, 2, 150, 150, dt, scale, True, 32)
+    check_bwd("scale %g" % scale, dt, got, ref, g64)
