@@ -15,7 +15,7 @@ import math
 import numpy as np
 import pytest
 
-from exact_attention_fa2_amd import workloads
+from exact_attention_fa2_amd import fa2, workloads
 from test_gpu_bwd import check as check_bwd
 from test_gpu_bwd import run as run_bwd
 from test_gpu_fwd import check_full
@@ -156,3 +156,36 @@ def test_forward_unusual_scales(scale, causal, dt, D):
 def test_backward_unusual_scales(scale, dt):
     got, ref, g64 = run_bwd(1, 2, 150, 150, dt, scale, True, 32)
     check_bwd("scale %g" % scale, dt, got, ref, g64)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 2.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_unusual_scales_without_workspace(scale, causal):
+    """The same for the float32 16-row kernel (no workspace, no key split)."""
+    import torch
+    from gpu_util import LSE_TOL, TOL, assert_close, download_f64, seeded, upload
+    import oracle
+    from exact_attention_fa2_amd import inputs
+    q, k, v = seeded(1, 2, 300, 300, 64, "f32", 33)
+    o, lse = fa2.attn_fwd(upload(q, "f32"), upload(k, "f32"), upload(v, "f32"), scale=scale,
+                          causal=causal, return_lse=True, use_workspace=False)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn(*(inputs.to_f64(x, "f32") for x in (q, k, v)), scale, causal)
+    assert_close("f32 no workspace scale %g O" % scale, download_f64(o), ro, TOL["f32"])
+    assert_close("f32 no workspace scale %g LSE" % scale, download_f64(lse), rl, LSE_TOL)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("scale", [0.0, -0.09, 1.5])
+def test_decode_unusual_scales(scale, dt):
+    """Flash-decoding with the same scales.  A large scale makes the softmax
+    peaky and |O| passes 2, where half a bf16 spacing (2^-7) exceeds the plain
+    4e-3 bar: bf16 takes the output-rounding bound of gpu_util.edge_tol."""
+    import oracle
+    from exact_attention_fa2_amd import inputs
+    from gpu_util import assert_close, edge_tol
+    from test_gpu_decode import run as run_decode
+    (q, k, v, _), o, *_ = run_decode(2, 3, 777, 128, dt, 5, seed=34, scale=scale)
+    q64, k64, v64 = (inputs.to_f64(x, dt) for x in (q, k, v))
+    ref = oracle.attn(q64[:, :, None], k64, v64, scale)[0][:, :, 0]
+    assert_close("decode scale %g %s" % (scale, dt), o, ref, edge_tol(dt, ref, o))
