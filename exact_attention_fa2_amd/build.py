@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfa2.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "fwd_f32.hip", "fwd_mfma.hip", "decode.hip", "bwd.hip"]
+SOURCES = ["api.cpp", "fwd_f32.hip", "fwd_mfma.hip", "decode.hip", "bwd.hip", "bwd_f32.hip"]
 ARCH = "gfx950"
 
 COMMON = [
@@ -61,7 +61,7 @@ def build(asm_dir: str | None = None, verbose: bool = False) -> str:
             print(msg, file=sys.stderr)
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = OUT + ".tmp%d" % os.getpid()
     cmd = [hipcc, "-shared", "-o", tmp] + objs + ["--offload-arch=" + ARCH, "-fPIC"]

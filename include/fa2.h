@@ -135,13 +135,16 @@ size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int causal, 
  *   delta       [B,H,Nq] float32: output (the library fills it and then
  *               reads it; its contents on entry are ignored)
  *   causal, scale  as in attn_fwd (causal requires Nq == Nk)
- *   Arithmetic: the four products per block run on MFMA with float32
- *   accumulation; P and dS are rounded to dtype before the two products
- *   that consume them (as P is in attn_fwd); delta, P and dS are formed in
- *   float32.  With Nq == 0, dk and dv are set to zero.
- *   Supported: D == 64 or 128; dtype F16, BF16 (F32 -> FA2_ERR_UNSUPPORTED);
- *   any B, H, Nq >= 0 (B*H == 0 enqueues nothing); Nk >= 1;
- *   B*H*ceil(max(Nq,Nk) / W) < 2^24 with W = 128 (D = 64) or 64 (D = 128).
+ *   Arithmetic: the products per block run on MFMA with float32
+ *   accumulation.  F16/BF16: P and dS are rounded to dtype before the two
+ *   products that consume them (as P is in attn_fwd); delta, P and dS are
+ *   formed in float32.  F32: float32 MFMA operands, nothing is rounded to a
+ *   narrower type.  With Nq == 0, dk and dv are set to zero.  The results do
+ *   not depend on timing (no atomics): equal inputs give equal bits.
+ *   Supported: D == 64 or 128 with F16 or BF16, D == 64 with F32 (F32 with
+ *   D == 128 -> FA2_ERR_UNSUPPORTED); any B, H, Nq >= 0 (B*H == 0 enqueues
+ *   nothing); Nk >= 1; B*H*ceil(max(Nq,Nk) / W) < 2^24 with W = 128
+ *   (D = 64) or 64 (D = 128).
  */
 fa2_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
                     const void *dout, const float *lse, void *dq, void *dk, void *dv,
