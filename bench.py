@@ -128,9 +128,10 @@ def extra_cases():
     Forward: the multi-head f16/bf16 shape (no LSE), the causal f16 workload
     (with LSE, causal and not), and the generalised prefill shapes (D = 128,
     a ragged N = 2000, Nq != Nk).  Backward: attn_bwd alone on the multi-head
-    N = 2048 shape (f16, bf16, causal f16, and f16 at D = 128; O and the LSE
-    from one untimed attn_fwd), 10*Nq*Nk*D flops per head (five products),
-    halved when causal."""
+    N = 2048 shape (f16, bf16, causal f16, and f16 at D = 128) and on the
+    single-head f32 N = 4096 shape (O and the LSE from one untimed attn_fwd),
+    10*Nq*Nk*D flops per head (five products), halved when causal; the f32
+    case is rated against the f32 peak."""
     import dataclasses
 
     import torch
@@ -162,6 +163,7 @@ def extra_cases():
            for dt, causal in (("f16", False), ("bf16", False), ("f16", True))]
     bwd.append(workloads.Prefill("B4 H12 M=N=2048 D128 f16", 4, 12, 2048, 2048, 128, "f16",
                                  1 / math.sqrt(128), False, 0))
+    bwd.append(workloads.HEADLINE_F32)
     for cfg in bwd:
         dt, causal = cfg.dtype, cfg.causal
         q, k, v = prefill_inputs(cfg)
@@ -172,7 +174,7 @@ def extra_cases():
         yield ("bwd %s%s" % (cfg.name, " causal" if causal else ""),
                lambda: fa2.attn_bwd(q, k, v, o, g, lse, scale=cfg.scale, causal=causal, dq=dq_,
                                     dk=dk_, dv=dv_, delta=delta),
-               2.5 * cfg.flops, {}, 20)
+               2.5 * cfg.flops, {"peak_tflops": PEAK_F32} if dt == "f32" else {}, 20)
         del q, k, v, g, o, lse, dq_, dk_, dv_, delta
 
 
@@ -266,10 +268,11 @@ def main():
         for name, call, flops, info, calls in extra_cases():
             ms = time_median(call, calls=calls)
             tf = flops / (ms * 1e-3) / 1e12
+            peak = info.get("peak_tflops", PEAK_F16)
             extra[name] = dict({"us": round(ms * 1e3, 2), "tflops": round(tf, 2),
-                                "frac_of_mfma_peak": round(tf / PEAK_F16, 4)}, **info)
+                                "frac_of_mfma_peak": round(tf / peak, 4)}, **info)
             log("%s: %.2f us, %.1f TFLOP/s (%.1f%% of MFMA peak)" % (name, ms * 1e3, tf,
-                                                                     100 * tf / PEAK_F16))
+                                                                     100 * tf / peak))
         torch.cuda.empty_cache()
 
     pq, pk, pv = prefill_inputs(pre)
