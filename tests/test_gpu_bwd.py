@@ -19,7 +19,13 @@ below u.  Each rounding is a relative error of at most u on one term, so
   * where a gradient is exactly zero (one key: dS = dP - D cancels) the
     float32 difference of two 64-term dot products is left: an absolute
     floor of 1e-5 covers it, and the relative L2 check is skipped for
-    tensors whose largest entry is below 1e-3.
+    tensors whose largest entry is below 1e-3;
+  * the relative L2 bound rests on many independent errors averaging out,
+    so it applies only where each entry sums at least 16 terms (dQ: keys,
+    dK and dV: queries).  With two keys, dQ_1 = scale dS_10 (k_0 - k_1) and
+    dS_10 carries the error of D, which is formed from the rounded O: when
+    the entry nearly cancels, its relative error is not bounded by u and only
+    the max-abs bound holds.
 """
 import numpy as np
 import pytest
@@ -60,14 +66,15 @@ def run(B, H, Nq, Nk, dt, scale, causal, seed, heads=None, D=64):
 
 def check(name, dt, got, ref, g64):
     u = U[dt]
-    for label, x, r in zip(("dQ", "dK", "dV"), got[:3], ref[:3]):
+    nq, nk = ref[0].shape[1], ref[1].shape[1]
+    for label, x, r, terms in zip(("dQ", "dK", "dV"), got[:3], ref[:3], (nk, nq, nq)):
         if r.size == 0:
             continue
         e, msg = report("%s %s" % (name, label), x, r)
         assert np.all(np.isfinite(x)), msg
         scale_ = float(np.abs(r).max())
         assert e <= 4 * u * scale_ + FLOOR, msg + " > 4u max|ref| = %.3e" % (4 * u * scale_)
-        if scale_ >= 1e-3:
+        if scale_ >= 1e-3 and terms >= 16:
             rel = float(np.linalg.norm(x - r) / np.linalg.norm(r))
             assert rel <= 2 * u, msg + " rel L2 %.3e > 2u" % rel
     if ref[3].size:
