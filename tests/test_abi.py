@@ -170,3 +170,13 @@ def test_bwd_error_paths():
     assert _bwd(B=300, H=300) == 3
     # B*H == 0: a valid no-op, even with NULL pointers
     assert fa2.lib().attn_bwd(*([None] * 10), 0, 4, 4, 4, 64, 0.1, 0, 1, None) == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The path has no multi-GPU form: bench.py --gpus N with N > 1 exits with
+    a message before touching a GPU."""
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
