@@ -355,7 +355,7 @@ def main():
         },
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_F32,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_F32, 4),
-                     "traffic": traffic.get("fwd_f32"), "kernel": "fwd_f32_d64",
+                     "traffic": traffic.get("fwd_f32"), "kernel": "fwd_f32_rows_kernel<64, false>",
                      "us": round(pre_ms * 1e3, 3)},
         "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "us": round(dec_ms * 1e3, 2),
                    "split_us": round(split_ms * 1e3, 2), "combine_us": round(comb_ms * 1e3, 2),

@@ -55,7 +55,7 @@ fa2_status fwd_impl(const void *q, const void *k, const void *v, void *o, float 
     if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
     if (causal != 0 && causal != 1) return FA2_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return FA2_ERR_UNSUPPORTED;
-    if (D != 64 && !(D == 128 && dtype != FA2_F32)) return FA2_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return FA2_ERR_UNSUPPORTED;
     if (causal && Nq != Nk) return FA2_ERR_UNSUPPORTED;
     if ((long long)B * H * Nq == 0) return FA2_OK;  // nothing to compute
     if (!q || !k || !v || !o) return FA2_ERR_NULL;
@@ -71,7 +71,7 @@ fa2_status fwd_impl(const void *q, const void *k, const void *v, void *o, float 
     fa2::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dev->num_cus,
                    workspace, workspace ? workspace_bytes : 0};
     hipStream_t st = (hipStream_t)stream;
-    if (dtype == FA2_F32) return fa2::launch_fwd_f32_d64(a, st);
+    if (dtype == FA2_F32) return fa2::launch_fwd_f32(a, st);
     return fa2::launch_fwd_mfma(a, dtype, st);
 }
 
@@ -94,12 +94,12 @@ FA2_API fa2_status attn_fwd_ws(const void *q, const void *k, const void *v, void
 FA2_API size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int causal,
                                        fa2_dtype dtype) {
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || !valid_dtype(dtype)) return 0;
-    if (D != 64 && !(D == 128 && dtype != FA2_F32)) return 0;
+    if (D != 64 && D != 128) return 0;
     if (causal && Nq != Nk) return 0;
     if ((long long)B * H > 65535) return 0;
     int cus = 256;
     if (const DeviceInfo *dev = current_device()) cus = dev->num_cus;
-    if (dtype == FA2_F32) return fa2::f32_workspace_bytes(B, H, Nq, Nk, cus);
+    if (dtype == FA2_F32) return fa2::f32_workspace_bytes(B, H, Nq, Nk, D, cus);
     return fa2::mfma_workspace_bytes(B, H, Nq, Nk, D, causal, cus);
 }
 

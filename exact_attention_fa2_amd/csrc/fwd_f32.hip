@@ -61,28 +61,42 @@ inline dim3 tile_grid(long long n_qtiles, long long n_bh, int chunks) {
     return dim3((unsigned)(n_qtiles * n_bh), 1, (unsigned)chunks);
 }
 
-struct KVRegs {
-    f32x4 k[4];   // k[j] = K[key k0 + c][16j + 4g .. 16j + 4g + 3]
-    f32x4 v[4];   // v[t] = V[key k0 + 4g + t][4c .. 4c+3], t = 0..3
-};
-
-__device__ __forceinline__ void load_kv(KVRegs &r, __amdgpu_buffer_rsrc_t rk,
-                                        __amdgpu_buffer_rsrc_t rv, int k0, int g, int c) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        r.k[j] = __builtin_bit_cast(f32x4, load16(rk, (uint32_t)(((k0 + c) * kD + 16 * j + 4 * g) * 4)));
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-        r.v[t] = __builtin_bit_cast(f32x4, load16(rv, (uint32_t)(((k0 + 4 * g + t) * kD + 4 * c) * 4)));
+// Waves of the 16-row kernel: at D = 64, 16 (four per SIMD, 128 registers
+// each); at D = 128 the K/V operands double, so 8 (two per SIMD, 256).
+template <int D>
+constexpr int rows_waves() {
+    return D == 64 ? 16 : 8;
 }
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
+template <int D>
+struct KVRegs {
+    f32x4 k[D / 16];     // k[j] = K[key k0 + c][16j + 4g .. 16j + 4g + 3]
+    f32x4 v[4][D / 64];  // v[t][h] = V[key k0 + 4g + t][64h + 4c .. 64h + 4c + 3], t = 0..3
+};
+
+template <int D>
+__device__ __forceinline__ void load_kv(KVRegs<D> &r, __amdgpu_buffer_rsrc_t rk,
+                                        __amdgpu_buffer_rsrc_t rv, int k0, int g, int c) {
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+        r.k[j] = __builtin_bit_cast(f32x4, load16(rk, (uint32_t)(((k0 + c) * D + 16 * j + 4 * g) * 4)));
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int h = 0; h < D / 64; ++h)
+            r.v[t][h] = __builtin_bit_cast(
+                f32x4, load16(rv, (uint32_t)(((k0 + 4 * g + t) * D + 64 * h + 4 * c) * 4)));
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     float *__restrict__ O, float *__restrict__ LSE, int Nq, int Nk, float scale_log2) {
-    __shared__ __attribute__((aligned(16))) float s_o[kWaves][kQT][kD];
-    __shared__ float s_m[kWaves][kQT];
-    __shared__ float s_l[kWaves][kQT];
+    constexpr int W = rows_waves<D>();
+    constexpr int NH = D / 64;  // 64-column halves of O
+    __shared__ __attribute__((aligned(16))) float s_o[W][kQT][D];
+    __shared__ float s_m[W][kQT];
+    __shared__ float s_l[W][kQT];
 
     const int lane = threadIdx.x & 63;
     // wave index as a wave-uniform value, so the key loop below is scalar
@@ -92,21 +106,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
     tile_of<CAUSAL>((Nq + kQT - 1) / kQT, qt, bh);
     const int q0 = qt * kQT;
 
-    const float *Qh = Q + (size_t)bh * Nq * kD;
-    const float *Kh = K + (size_t)bh * Nk * kD;
-    const float *Vh = V + (size_t)bh * Nk * kD;
-    const auto rq = make_rsrc(Qh, (uint32_t)Nq * kD * 4);
-    const auto rk = make_rsrc(Kh, (uint32_t)Nk * kD * 4);
-    const auto rv = make_rsrc(Vh, (uint32_t)Nk * kD * 4);
+    const float *Qh = Q + (size_t)bh * Nq * D;
+    const float *Kh = K + (size_t)bh * Nk * D;
+    const float *Vh = V + (size_t)bh * Nk * D;
+    const auto rq = make_rsrc(Qh, (uint32_t)Nq * D * 4);
+    const auto rk = make_rsrc(Kh, (uint32_t)Nk * D * 4);
+    const auto rv = make_rsrc(Vh, (uint32_t)Nk * D * 4);
 
     // Q^T operand of S^T = K Q^T: slot i of lane (g,c) is Q[q0 + c][d(g,i)]
     // with d(g,i) = 16*(i/4) + 4g + i%4 -- any pairing of the contraction index
     // works, and this one lets the four lanes of a key row read 64 contiguous
     // bytes of K per load instruction.
-    float qv[16];
+    float qv[D / 4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        f32x4 t = __builtin_bit_cast(f32x4, load16(rq, (uint32_t)(((q0 + c) * kD + 16 * j + 4 * g) * 4)));
+    for (int j = 0; j < D / 16; ++j) {
+        f32x4 t = __builtin_bit_cast(f32x4, load16(rq, (uint32_t)(((q0 + c) * D + 16 * j + 4 * g) * 4)));
         qv[4 * j + 0] = t[0];
         qv[4 * j + 1] = t[1];
         qv[4 * j + 2] = t[2];
@@ -115,15 +129,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
 
     const int kend = CAUSAL ? min(Nk, q0 + kQT) : Nk;
     const int nsteps = (kend + kStep - 1) / kStep;
-    const int per = (nsteps + kWaves - 1) / kWaves;
+    const int per = (nsteps + W - 1) / W;
     const int st0 = wave * per;
     const int st1 = min(nsteps, st0 + per);
 
     float m = -INFINITY;  // running max of scaled scores, base-2 units
     float l = 0.f;        // this lane's share of the running denominator
-    f32x4 acc[4];
+    f32x4 acc[4 * NH];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4 * NH; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // One 16-key step on the registers in `cur`; the next step's K/V are
     // loaded into `nxt` first so the loads overlap this step's work.  The load
@@ -131,9 +145,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
     // keys, harmlessly: in-slice data or zeros from the buffer descriptor), so
     // the compiler's count of loads in flight is the same on every path and its
     // wait for `cur` never also waits for `nxt`.
-    auto step = [&](int st, const KVRegs &cur, KVRegs &nxt) {
+    auto step = [&](int st, const KVRegs<D> &cur, KVRegs<D> &nxt) {
         const int k0 = st * kStep;
-        load_kv(nxt, rk, rv, k0 + kStep, g, c);
+        load_kv<D>(nxt, rk, rv, k0 + kStep, g, c);
         // keep the loads here: without this the scheduler sinks them next to
         // their use in the following step, which serialises load and compute
         __builtin_amdgcn_sched_barrier(0);
@@ -141,7 +155,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
         // two independent accumulation chains, summed at the end
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, sacc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
+        for (int i = 0; i < D / 4; i += 2) {
             sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.k[i >> 2][i & 3], qv[i], sacc, 0, 0, 0);
             sacc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.k[i >> 2][(i & 3) + 1], qv[i + 1], sacc2,
                                                         0, 0, 0);
@@ -170,7 +184,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
             const float corr = exp2f_fast(m - m_use);
             l *= corr;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] *= corr;
+            for (int j = 0; j < 4 * NH; ++j) acc[j] *= corr;
         }
         float p[4];
         float psum = 0.f;
@@ -180,25 +194,30 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
             psum += p[r];
         }
         l += psum;
-        // O^T += V^T P^T: slot g pairs key k0 + 4g + t; row m of tile j is d = 4m + j.
+        // O^T += V^T P^T: slot g pairs key k0 + 4g + t; row m of tile 4h + j is
+        // d = 64h + 4m + j.
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.v[t][j], p[t], acc[j], 0, 0, 0);
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[4 * h + j] =
+                        __builtin_amdgcn_mfma_f32_16x16x4f32(cur.v[t][h][j], p[t], acc[4 * h + j], 0, 0, 0);
         m = m_new;
     };
 
     // Steps run in pairs, unconditionally, so each step's prefetch has a
     // use on every path and the compiler keeps it where it is issued.
-    KVRegs ra, rb;
-    load_kv(ra, rk, rv, st0 * kStep, g, c);
+    KVRegs<D> ra, rb;
+    load_kv<D>(ra, rk, rv, st0 * kStep, g, c);
     for (int st = st0; st < st1; st += 2) {
         step(st, ra, rb);
         step(st + 1, rb, ra);
     }
 
-    // acc[j][r] = O[q0 + c][16g + 4r + j]; the lane's l covers keys 4g..4g+3 of each step.
+    // acc[4h + j][r] = O[q0 + c][64h + 16g + 4r + j]; the lane's l covers keys
+    // 4g..4g+3 of each step.
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (g == 0) {
@@ -206,29 +225,34 @@ __global__ __launch_bounds__(kWaves * 64, 1) void fwd_f32_d64_kernel(
         s_l[wave][c] = l;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<f32x4 *>(&s_o[wave][c][16 * g + 4 * r]) =
-            f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<f32x4 *>(&s_o[wave][c][64 * h + 16 * g + 4 * r]) =
+                f32x4{acc[4 * h][r], acc[4 * h + 1][r], acc[4 * h + 2][r], acc[4 * h + 3][r]};
     __syncthreads();
 
-    // Merge the 16 wave states of each row: one output element per thread.
-    const int row = threadIdx.x >> 6;
-    const int d = threadIdx.x & 63;
-    float mg = -INFINITY;
+    // Merge the wave states of each row: one output element per thread and
+    // pass (one pass at D = 64, four at D = 128).
+    for (int e = threadIdx.x; e < kQT * D; e += W * 64) {
+        const int row = e / D;
+        const int d = e % D;
+        float mg = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mg = fmaxf(mg, s_m[w][row]);
-    float lg = 0.f, o0 = 0.f;
+        for (int w = 0; w < W; ++w) mg = fmaxf(mg, s_m[w][row]);
+        float lg = 0.f, o0 = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const float mw = s_m[w][row];
-        const float wt = mw == -INFINITY ? 0.f : exp2f_fast(mw - mg);
-        lg += wt * s_l[w][row];
-        o0 += wt * s_o[w][row][d];
-    }
-    const int qrow = q0 + row;
-    if (qrow < Nq) {
-        O[((size_t)bh * Nq + qrow) * kD + d] = o0 / lg;
-        if (LSE && d == 0) LSE[(size_t)bh * Nq + qrow] = (mg + log2f_fast(lg)) * kLn2;
+        for (int w = 0; w < W; ++w) {
+            const float mw = s_m[w][row];
+            const float wt = mw == -INFINITY ? 0.f : exp2f_fast(mw - mg);
+            lg += wt * s_l[w][row];
+            o0 += wt * s_o[w][row][d];
+        }
+        const int qrow = q0 + row;
+        if (qrow < Nq) {
+            O[((size_t)bh * Nq + qrow) * D + d] = o0 / lg;
+            if (LSE && d == 0) LSE[(size_t)bh * Nq + qrow] = (mg + log2f_fast(lg)) * kLn2;
+        }
     }
 }
 
@@ -495,7 +519,8 @@ int f32_chunks(int B, int H, int Nq, int Nk, int num_cus) {
     return (int)std::max<long long>(1, c);
 }
 
-size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int num_cus) {
+size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int D, int num_cus) {
+    if (D != kD) return 0;  // D = 128 always runs the 16-row kernel
     const int c = f32_chunks(B, H, Nq, Nk, num_cus);
     if (c <= 1) return 0;
     return (size_t)B * H * Nq * c * (kD + 2) * sizeof(float);
@@ -505,10 +530,23 @@ size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int num_cus) {
 #define FA2_F32_SHARED 1
 #endif
 
-fa2_status launch_fwd_f32_d64(const FwdArgs &a, hipStream_t st) {
+template <int D>
+fa2_status launch_rows(const FwdArgs &a, float sl2, hipStream_t st) {
+    const dim3 grid = tile_grid((a.Nq + kQT - 1) / kQT, a.B * a.H, 1);
+    const dim3 block(rows_waves<D>() * 64);
+    auto k = a.causal ? fwd_f32_rows_kernel<D, true> : fwd_f32_rows_kernel<D, false>;
+    return launch(k, grid, block, st, (const float *)a.q, (const float *)a.k, (const float *)a.v,
+                  (float *)a.o, a.lse, a.Nq, a.Nk, sl2);
+}
+
+fa2_status launch_fwd_f32(const FwdArgs &a, hipStream_t st) {
     // one-dimensional grids of 16-row tiles (the most numerous) must fit a grid dimension
     if ((long long)a.B * a.H * ((a.Nq + kQT - 1) / kQT) > 0x7FFFFFFFLL) return FA2_ERR_UNSUPPORTED;
     const float sl2 = a.scale * kLog2e;
+    // D = 128: the 16-row kernel at two waves per SIMD for every shape (the
+    // shared-K/V kernel holds the operands of four query tiles per wave group
+    // and has no registers for twice the columns)
+    if (a.D == 128) return launch_rows<128>(a, sl2, st);
     const long long groups = (long long)a.B * a.H * ((a.Nq + shared::kRows - 1) / shared::kRows);
     const dim3 block(kWaves * 64);
     if (FA2_F32_SHARED && groups >= a.num_cus) {
@@ -520,7 +558,7 @@ fa2_status launch_fwd_f32_d64(const FwdArgs &a, hipStream_t st) {
                       a.Nq, a.Nk, sl2);
     }
     const int c = f32_chunks(a.B, a.H, a.Nq, a.Nk, a.num_cus);
-    if (c > 1 && a.ws && a.ws_bytes >= f32_workspace_bytes(a.B, a.H, a.Nq, a.Nk, a.num_cus)) {
+    if (c > 1 && a.ws && a.ws_bytes >= f32_workspace_bytes(a.B, a.H, a.Nq, a.Nk, kD, a.num_cus)) {
         // few rows: split the keys into c chunks, then merge the partials
         const size_t rows = (size_t)a.B * a.H * a.Nq;
         float *o_part = (float *)a.ws;
@@ -535,12 +573,7 @@ fa2_status launch_fwd_f32_d64(const FwdArgs &a, hipStream_t st) {
         return launch_combine_rows(o_part, m_part, l_part, a.o, a.lse, rows, kD, c, FA2_F32, st);
     }
     // few rows and no workspace: 16-row workgroups fill the device instead
-    const dim3 grid = tile_grid((a.Nq + kQT - 1) / kQT, a.B * a.H, 1);
-    if (a.causal)
-        return launch(fwd_f32_d64_kernel<true>, grid, block, st, (const float *)a.q,
-                      (const float *)a.k, (const float *)a.v, (float *)a.o, a.lse, a.Nq, a.Nk, sl2);
-    return launch(fwd_f32_d64_kernel<false>, grid, block, st, (const float *)a.q,
-                  (const float *)a.k, (const float *)a.v, (float *)a.o, a.lse, a.Nq, a.Nk, sl2);
+    return launch_rows<kD>(a, sl2, st);
 }
 
 }  // namespace fa2

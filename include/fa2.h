@@ -75,9 +75,9 @@ typedef enum {
  *   both products on MFMA with P rounded to the input dtype; float32 inputs
  *   run both products on float32 MFMA (no reduced-precision rounding).
  *   o is rounded to nearest-even into dtype.
- *   Supported: D == 64 with dtype F32, F16 or BF16, and D == 128 with F16 or
- *   BF16; any B, H, Nq >= 0 (zero-size outputs enqueue nothing); Nk >= 1;
- *   ragged Nq/Nk are masked in the tail.
+ *   Supported: D == 64 or 128 with dtype F32, F16 or BF16; any B, H,
+ *   Nq >= 0 (zero-size outputs enqueue nothing); Nk >= 1; ragged Nq/Nk are
+ *   masked in the tail.
  */
 fa2_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                     int B, int H, int Nq, int Nk, int D, float scale, int causal,

@@ -1,5 +1,5 @@
-"""GPU parity of attn_fwd with head dimension 128 (f16/bf16) against the fp64
-oracle, through the C ABI.
+"""GPU parity of attn_fwd with head dimension 128 (f16, bf16 and f32) against
+the fp64 oracle, through the C ABI.
 
 Same bars as D = 64: 4e-3 max abs on O for the multi-head N(0,1) shapes, the
 format bound of gpu_util.edge_tol for ragged and few-key cases, 1e-4 on the
@@ -21,7 +21,7 @@ D = 128
 SCALE = 1.0 / math.sqrt(D)
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 def test_multihead_1024_full(dt):
     check_full(workloads.Prefill("B4 H12 N1024 D128 %s" % dt, 4, 12, 1024, 1024, D, dt, SCALE,
                                  False, 21))
@@ -57,7 +57,7 @@ RAGGED = [  # (B, H, Nq, Nk, causal)
 ]
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
 def test_ragged_and_degenerate(shape, dt):
     B, H, Nq, Nk, causal = shape
@@ -92,7 +92,7 @@ def test_split_schedules(shape, dt):
         assert_close("split %s LSE" % tag, download_f64(lse), rl, LSE_TOL)
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_zero_keys_give_mean_of_values(dt, causal):
     """K = 0: every score is 0, so O is the mean of the live V rows (the

@@ -36,7 +36,7 @@ def _forward_cases(n=96, seed=2024):
     out = []
     for i in range(n):
         dt = ("f32", "f16", "bf16")[i % 3]
-        D = 64 if dt == "f32" else int(g.choice([64, 128]))
+        D = int(g.choice([64, 128]))
         causal = bool(g.integers(2))
         B, H = int(g.integers(1, 4)), int(g.integers(1, 5))
         Nq = _length(g, 2000)
@@ -70,7 +70,7 @@ def _large_forward_cases(n=30, seed=7):
     out = []
     for i in range(n):
         dt = ("f32", "f16", "bf16")[i % 3]
-        D = 64 if dt == "f32" else int(g.choice([64, 128]))
+        D = int(g.choice([64, 128]))
         causal = bool(g.integers(2))
         B, H = int(g.integers(1, 9)), int(g.integers(1, 33))
         Nq = int(g.integers(128, 4097))
@@ -139,8 +139,8 @@ def test_backward_large(case):
     check_bwd("random " + _id(case), dt, got, ref, g64)
 
 
-@pytest.mark.parametrize("dt,D", [("f32", 64), ("f16", 64), ("bf16", 64), ("f16", 128),
-                                  ("bf16", 128)])
+@pytest.mark.parametrize("dt,D", [("f32", 64), ("f16", 64), ("bf16", 64), ("f32", 128),
+                                  ("f16", 128), ("bf16", 128)])
 @pytest.mark.parametrize("scale", [0.0, -0.125, 2.0])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_unusual_scales(scale, causal, dt, D):
