@@ -93,17 +93,19 @@ def _validate(ref, specs):
     library cannot see buffer sizes, so a short buffer would be overrun).
     ``specs`` holds (tensor, name, shape, dtype); shape None checks only the
     rest (a byte workspace)."""
+    # (cheap attribute checks first: these run on every call)
     for t, name, shape, dtype in specs:
-        if shape is not None and tuple(t.shape) != tuple(shape):
+        if shape is not None and t.shape != shape:
             raise ValueError("%s must have shape %s, not %s" % (name, tuple(shape), tuple(t.shape)))
         if dtype is not None and t.dtype != dtype:
             raise TypeError("%s must be %s, not %s" % (name, dtype, t.dtype))
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
-    if ref.device.type != "cuda":
+    dev = ref.get_device()  # -1 on the host
+    if dev < 0:
         raise ValueError("tensors must be on a GPU, not %s" % ref.device)
     for t, name, _, _ in specs:
-        if t.device != ref.device:
+        if t.get_device() != dev:
             raise ValueError("%s must be on %s, not %s" % (name, ref.device, t.device))
 
 
@@ -129,8 +131,14 @@ def attn_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=
     torch = _torch()
     B, H, Nq, D = _dims(q, 4, "q")
     Nk = _dims(k, 4, "k")[2]
-    _validate(q, [(q, "q", (B, H, Nq, D), q.dtype), (k, "k", (B, H, Nk, D), q.dtype),
-                  (v, "v", (B, H, Nk, D), q.dtype)])
+    # buffers the binding allocates below are right by construction; the
+    # caller's are checked with the inputs
+    specs = [(q, "q", None, None), (k, "k", (B, H, Nk, D), q.dtype), (v, "v", (B, H, Nk, D), q.dtype)]
+    if out is not None:
+        specs.append((out, "out", q.shape, q.dtype))
+    if return_lse and lse is not None:
+        specs.append((lse, "lse", (B, H, Nq), torch.float32))
+    _validate(q, specs)
     dc = dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -138,10 +146,6 @@ def attn_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    outs = [(out, "out", (B, H, Nq, D), q.dtype)]
-    if return_lse:
-        outs.append((lse, "lse", (B, H, Nq), torch.float32))
-    _validate(q, outs)
     if not use_workspace:
         st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
                             _ptr(lse if return_lse else None), B, H, Nq, Nk, D, float(scale),
@@ -171,9 +175,13 @@ def attn_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, 
     B, H, Nq, D = _dims(q, 4, "q")
     Nk = _dims(k, 4, "k")[2]
     qs, ks, f32 = (B, H, Nq, D), (B, H, Nk, D), torch.float32
-    _validate(q, [(q, "q", qs, q.dtype), (k, "k", ks, q.dtype), (v, "v", ks, q.dtype),
-                  (o, "o", qs, q.dtype), (dout, "dout", qs, q.dtype),
-                  (lse, "lse", (B, H, Nq), f32)])
+    specs = [(q, "q", None, None), (k, "k", ks, q.dtype), (v, "v", ks, q.dtype),
+             (o, "o", qs, q.dtype), (dout, "dout", qs, q.dtype), (lse, "lse", (B, H, Nq), f32)]
+    for t, name, shape, dtype in ((dq, "dq", qs, q.dtype), (dk, "dk", ks, q.dtype),
+                                  (dv, "dv", ks, q.dtype), (delta, "delta", (B, H, Nq), f32)):
+        if t is not None:
+            specs.append((t, name, shape, dtype))
+    _validate(q, specs)
     dc = dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -182,8 +190,6 @@ def attn_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, 
     dv = torch.empty_like(v) if dv is None else dv
     if delta is None:
         delta = torch.empty((B, H, Nq), dtype=f32, device=q.device)
-    _validate(q, [(dq, "dq", qs, q.dtype), (dk, "dk", ks, q.dtype), (dv, "dv", ks, q.dtype),
-                  (delta, "delta", (B, H, Nq), f32)])
     st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                         _ptr(dk), _ptr(dv), _ptr(delta), B, H, Nq, Nk, D, float(scale),
                         int(bool(causal)), dc, _stream(stream))
@@ -200,8 +206,13 @@ def attn_decode_split(q, k, v, scale, n_splits, o_part=None, m_part=None, l_part
     n_splits = int(n_splits)
     if n_splits < 1:
         raise ValueError("n_splits must be at least 1")
-    _validate(q, [(q, "q", (B, H, D), q.dtype), (k, "k", (B, H, N, D), q.dtype),
-                  (v, "v", (B, H, N, D), q.dtype)])
+    f32 = torch.float32
+    specs = [(q, "q", None, None), (k, "k", (B, H, N, D), q.dtype), (v, "v", (B, H, N, D), q.dtype)]
+    for t, name, shape in ((o_part, "o_part", (B, H, n_splits, D)),
+                           (m_part, "m_part", (B, H, n_splits)), (l_part, "l_part", (B, H, n_splits))):
+        if t is not None:
+            specs.append((t, name, shape, f32))
+    _validate(q, specs)
     dc = dtype_code(q)
     if o_part is None:
         o_part = torch.empty((B, H, n_splits, D), dtype=torch.float32, device=q.device)
@@ -209,10 +220,6 @@ def attn_decode_split(q, k, v, scale, n_splits, o_part=None, m_part=None, l_part
         m_part = torch.empty((B, H, n_splits), dtype=torch.float32, device=q.device)
     if l_part is None:
         l_part = torch.empty((B, H, n_splits), dtype=torch.float32, device=q.device)
-    f32 = torch.float32
-    _validate(q, [(o_part, "o_part", (B, H, n_splits, D), f32),
-                  (m_part, "m_part", (B, H, n_splits), f32),
-                  (l_part, "l_part", (B, H, n_splits), f32)])
     st = lib().attn_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(m_part),
                                  _ptr(l_part), B, H, N, D, float(scale), n_splits, dc,
                                  _stream(stream))
@@ -225,11 +232,13 @@ def attn_decode_combine(o_part, m_part, l_part, dtype, out=None, stream=None):
     torch = _torch()
     B, H, S, D = _dims(o_part, 4, "o_part")
     f32 = torch.float32
-    _validate(o_part, [(o_part, "o_part", (B, H, S, D), f32), (m_part, "m_part", (B, H, S), f32),
-                       (l_part, "l_part", (B, H, S), f32)])
+    specs = [(o_part, "o_part", None, f32), (m_part, "m_part", (B, H, S), f32),
+             (l_part, "l_part", (B, H, S), f32)]
+    if out is not None:
+        specs.append((out, "out", (B, H, D), dtype))
+    _validate(o_part, specs)
     if out is None:
         out = torch.empty((B, H, D), dtype=dtype, device=o_part.device)
-    _validate(o_part, [(out, "out", (B, H, D), dtype)])
     st = lib().attn_decode_combine(_ptr(o_part), _ptr(m_part), _ptr(l_part), _ptr(out), B, H,
                                    D, S, dtype_code(out), _stream(stream))
     _check("attn_decode_combine", st)
