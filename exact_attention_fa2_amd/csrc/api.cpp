@@ -111,7 +111,7 @@ FA2_API fa2_status attn_bwd(const void *q, const void *k, const void *v, const v
     if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
     if (causal != 0 && causal != 1) return FA2_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return FA2_ERR_UNSUPPORTED;
-    if ((D != 64 && D != 128) || (dtype == FA2_F32 && D != 64)) return FA2_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return FA2_ERR_UNSUPPORTED;
     if (causal && Nq != Nk) return FA2_ERR_UNSUPPORTED;
     if ((long long)B * H == 0) return FA2_OK;
     if (!k || !v || !dk || !dv) return FA2_ERR_NULL;
@@ -130,7 +130,7 @@ FA2_API fa2_status attn_bwd(const void *q, const void *k, const void *v, const v
         return FA2_ERR_UNSUPPORTED;
     if (!current_device()) return FA2_ERR_DEVICE;
     fa2::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Nq, Nk, D, scale, causal};
-    if (dtype == FA2_F32) return fa2::launch_bwd_f32_d64(a, (hipStream_t)stream);
+    if (dtype == FA2_F32) return fa2::launch_bwd_f32(a, (hipStream_t)stream);
     return fa2::launch_bwd_mfma(a, dtype, (hipStream_t)stream);
 }
 

@@ -46,8 +46,8 @@ struct BwdArgs {
 
 // f16/bf16 backward on matrix cores, D = 64 or 128.
 fa2_status launch_bwd_mfma(const BwdArgs &a, fa2_dtype dt, hipStream_t st);
-// float32 backward on float32 matrix cores, D = 64.
-fa2_status launch_bwd_f32_d64(const BwdArgs &a, hipStream_t st);
+// float32 backward on float32 matrix cores, D = 64 or 128.
+fa2_status launch_bwd_f32(const BwdArgs &a, hipStream_t st);
 
 struct DecodeArgs {
     const void *q, *k, *v;

@@ -32,7 +32,7 @@ import pytest
 
 import oracle
 from exact_attention_fa2_amd import fa2, inputs
-from gpu_util import TOL, download_f64, report, upload
+from gpu_util import TOL, download_f64, report, torch_dtype, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -129,11 +129,11 @@ SMALL_D128 = [  # B, H, Nq, Nk, causal
 ]
 
 
-@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("B,H,Nq,Nk,causal", SMALL_D128)
 def test_bwd_parity_d128(B, H, Nq, Nk, causal, dt):
-    """Head dimension 128: two waves share each 32 keys of the dK/dV pass and
-    split its output columns; same bounds as D = 64."""
+    """Head dimension 128: two waves share each slice of queries in the dK/dV
+    pass and split its output columns; same bounds as D = 64."""
     scale = 1.0 / 128 ** 0.5
     name = "bwd D128 B%d H%d Nq%d Nk%d %s %s" % (B, H, Nq, Nk, dt, "causal" if causal else "full")
     print(name, flush=True)
@@ -141,7 +141,8 @@ def test_bwd_parity_d128(B, H, Nq, Nk, causal, dt):
     check(name, dt, got, ref, g64)
 
 
-@pytest.mark.parametrize("dt,causal", [("f16", False), ("bf16", False), ("f16", True)])
+@pytest.mark.parametrize("dt,causal", [("f16", False), ("bf16", False), ("f16", True),
+                                       ("f32", False), ("f32", True)])
 def test_bwd_d128_bench_shape_heads(dt, causal):
     heads = [0, 23, 47]
     name = "bwd B4 H12 N2048 D128 %s %s heads %s" % (dt, "causal" if causal else "full", heads)
@@ -150,14 +151,15 @@ def test_bwd_d128_bench_shape_heads(dt, causal):
     check(name, dt, got, ref, g64)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
-def test_bwd_no_queries(dt):
+def test_bwd_no_queries(dt, D):
     """Nq = 0: no query attends any key, so dK = dV = 0 exactly."""
     import torch
-    tdt = torch.float16 if dt == "f16" else torch.bfloat16
-    k = torch.randn(2, 3, 100, 64, device="cuda").to(tdt)
-    v = torch.randn(2, 3, 100, 64, device="cuda").to(tdt)
-    q = torch.empty(2, 3, 0, 64, device="cuda", dtype=tdt)
+    tdt = torch_dtype(dt)
+    k = torch.randn(2, 3, 100, D, device="cuda").to(tdt)
+    v = torch.randn(2, 3, 100, D, device="cuda").to(tdt)
+    q = torch.empty(2, 3, 0, D, device="cuda", dtype=tdt)
     lse = torch.empty(2, 3, 0, device="cuda")
     dk = torch.full_like(k, 7.0)
     dv = torch.full_like(v, 7.0)
@@ -166,27 +168,25 @@ def test_bwd_no_queries(dt):
     assert torch.count_nonzero(dk).item() == 0 and torch.count_nonzero(dv).item() == 0
 
 
-def test_bwd_rejects():
-    """f32 with D = 128, and D other than 64 and 128, are refused before
-    anything is enqueued."""
-    import torch
-    q = torch.zeros(1, 1, 8, 128, device="cuda")
-    lse = torch.zeros(1, 1, 8, device="cuda")
-    with pytest.raises(fa2.FA2Error) as e:
-        fa2.attn_bwd(q, q, q, q, q, lse)
-    assert e.value.status == 3
-    h = torch.zeros(1, 1, 8, 32, device="cuda", dtype=torch.float16)
-    with pytest.raises(fa2.FA2Error) as e:
-        fa2.attn_bwd(h, h, h, h, h, lse)
-    assert e.value.status == 3
-
-
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
-def test_bwd_deterministic(dt):
+def test_bwd_rejects(dt):
+    """D other than 64 and 128 is refused before anything is enqueued."""
+    import torch
+    lse = torch.zeros(1, 1, 8, device="cuda")
+    for D in (32, 96):
+        h = torch.zeros(1, 1, 8, D, device="cuda", dtype=torch_dtype(dt))
+        with pytest.raises(fa2.FA2Error) as e:
+            fa2.attn_bwd(h, h, h, h, h, lse)
+        assert e.value.status == 3
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
+def test_bwd_deterministic(dt, D):
     """No atomics: two runs give the same bits."""
     import torch
-    q, k, v = inputs.qkv((2, 3, 300, 64), (2, 3, 300, 64), 6, dt)
-    g = inputs.normal((2, 3, 300, 64), 6, 3, dt)
+    q, k, v = inputs.qkv((2, 3, 300, D), (2, 3, 300, D), 6, dt)
+    g = inputs.normal((2, 3, 300, D), 6, 3, dt)
     tq, tk, tv, tg = (upload(x, dt) for x in (q, k, v, g))
     o, lse = fa2.attn_fwd(tq, tk, tv, scale=0.125, causal=True, return_lse=True)
     a = fa2.attn_bwd(tq, tk, tv, o, tg, lse, scale=0.125, causal=True)

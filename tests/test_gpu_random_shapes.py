@@ -54,7 +54,7 @@ def _backward_cases(n=32, seed=77):
     out = []
     for i in range(n):
         dt = ("f16", "bf16", "f32")[i % 3]
-        D = 64 if dt == "f32" else int(g.choice([64, 128]))
+        D = int(g.choice([64, 128]))
         causal = bool(g.integers(2))
         B, H = int(g.integers(1, 3)), int(g.integers(1, 4))
         Nq = _length(g, 700)
@@ -85,7 +85,7 @@ def _large_backward_cases(n=12, seed=11):
     out = []
     for i in range(n):
         dt = ("f16", "bf16", "f32")[i % 3]
-        D = 64 if dt == "f32" else int(g.choice([64, 128]))
+        D = int(g.choice([64, 128]))
         causal = bool(g.integers(2))
         B, H = int(g.integers(1, 5)), int(g.integers(1, 17))
         Nq = int(g.integers(64, 2049))
@@ -151,10 +151,11 @@ def test_forward_unusual_scales(scale, causal, dt, D):
                edge=True)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("scale", [0.0, -0.125])
-def test_backward_unusual_scales(scale, dt):
-    got, ref, g64 = run_bwd(1, 2, 150, 150, dt, scale, True, 32)
+def test_backward_unusual_scales(scale, dt, D):
+    got, ref, g64 = run_bwd(1, 2, 150, 150, dt, scale, True, 32, D=D)
     check_bwd("scale %g" % scale, dt, got, ref, g64)
 
 
