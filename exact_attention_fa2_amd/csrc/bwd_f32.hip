@@ -54,32 +54,34 @@ struct Op {
     f32x4 x[N];
 };
 
-// Rows r0..r0+15 of a [N][D] tensor by rows (first products):
-//   x[j] = X[r0 + c][16j + 4g .. 16j + 4g + 3]
-template <int D>
-__device__ __forceinline__ void load_rows(Op<D / 16> &o, __amdgpu_buffer_rsrc_t r, int r0, int g,
-                                          int c) {
+// Rows r0..r0+15 of a tensor with rows of `ld` floats, by rows (first
+// products), N pieces from column col0 on:
+//   x[j] = X[r0 + c][col0 + 16j + 4g .. col0 + 16j + 4g + 3]
+template <int N>
+__device__ __forceinline__ void load_rows(Op<N> &o, __amdgpu_buffer_rsrc_t r, int r0, int ld,
+                                          int col0, int g, int c) {
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j)
-        o.x[j] = __builtin_bit_cast(f32x4, load16(r, (uint32_t)(((r0 + c) * D + 16 * j + 4 * g) * 4)));
+    for (int j = 0; j < N; ++j)
+        o.x[j] = __builtin_bit_cast(f32x4, load16(r, (uint32_t)(((r0 + c) * ld + col0 + 16 * j + 4 * g) * 4)));
 }
 
-// ... and by columns (second products), the 64-column block h of a [N][D]
-// tensor: x[t] = X[r0 + 4g + t][64h + 4c .. 64h + 4c + 3]
-template <int D>
-__device__ __forceinline__ void load_cols(Op<4> &o, __amdgpu_buffer_rsrc_t r, int r0, int h, int g,
-                                          int c) {
+// ... and by columns (second products), the 64 columns from col0 on:
+//   x[t] = X[r0 + 4g + t][col0 + 4c .. col0 + 4c + 3]
+__device__ __forceinline__ void load_cols(Op<4> &o, __amdgpu_buffer_rsrc_t r, int r0, int ld,
+                                          int col0, int g, int c) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-        o.x[t] = __builtin_bit_cast(f32x4, load16(r, (uint32_t)(((r0 + 4 * g + t) * D + 64 * h + 4 * c) * 4)));
+        o.x[t] = __builtin_bit_cast(f32x4, load16(r, (uint32_t)(((r0 + 4 * g + t) * ld + col0 + 4 * c) * 4)));
 }
 
-// B operand slots of row `row`: v[i] = X[row][16(i/4) + 4g + i%4].
-template <int D>
-__device__ __forceinline__ void load_bop(float *v, __amdgpu_buffer_rsrc_t r, int row, int g) {
+// B operand slots of row `row`, 16N columns from col0 on:
+//   v[i] = X[row][col0 + 16(i/4) + 4g + i%4]
+template <int N>
+__device__ __forceinline__ void load_bop(float *v, __amdgpu_buffer_rsrc_t r, int row, int ld,
+                                         int col0, int g) {
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-        const f32x4 t = __builtin_bit_cast(f32x4, load16(r, (uint32_t)((row * D + 16 * j + 4 * g) * 4)));
+    for (int j = 0; j < N; ++j) {
+        const f32x4 t = __builtin_bit_cast(f32x4, load16(r, (uint32_t)((row * ld + col0 + 16 * j + 4 * g) * 4)));
         v[4 * j + 0] = t[0];
         v[4 * j + 1] = t[1];
         v[4 * j + 2] = t[2];
@@ -91,12 +93,12 @@ __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// sum_i A_i B_i over the D/4 pairings of a D-long contraction, in two chains
-template <int D>
-__device__ __forceinline__ f32x4 product(const Op<D / 16> &a, const float *b) {
+// sum_i A_i B_i over the 4N pairings of a 16N-long contraction, in two chains
+template <int N>
+__device__ __forceinline__ f32x4 product(const Op<N> &a, const float *b) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < D / 4; i += 2) {
+    for (int i = 0; i < 4 * N; i += 2) {
         s = mfma(a.x[i >> 2][i & 3], b[i], s);
         s2 = mfma(a.x[i >> 2][(i & 3) + 1], b[i + 1], s2);
     }
@@ -157,8 +159,8 @@ __global__ __launch_bounds__(kW * 64, 1) void bwd_f32_dq_kernel(
     const auto rv = make_rsrc(V + (size_t)bh * Nk * D, (uint32_t)Nk * D * 4);
 
     float qv[D / 4], gv[D / 4];  // B operands: this lane's query row of Q and of dO
-    load_bop<D>(qv, rq, myq, g);
-    load_bop<D>(gv, rdo, myq, g);
+    load_bop<D / 16>(qv, rq, myq, D, 0, g);
+    load_bop<D / 16>(gv, rdo, myq, D, 0, g);
     const bool qlive = myq < Nq;
     const float l2 = qlive ? LSE[(size_t)bh * Nq + myq] * kLog2e : 0.f;  // L in base 2
     const float dl = qlive ? Delta[(size_t)bh * Nq + myq] : 0.f;
@@ -179,15 +181,15 @@ __global__ __launch_bounds__(kW * 64, 1) void bwd_f32_dq_kernel(
         Op<4> kc[NH];     // K by columns (dQ^T), per 64-column block
     };
     auto load = [&](Ops &o, int k0) {
-        load_rows<D>(o.k, rk, k0, g, c);
-        load_rows<D>(o.v, rv, k0, g, c);
+        load_rows(o.k, rk, k0, D, 0, g, c);
+        load_rows(o.v, rv, k0, D, 0, g, c);
 #pragma unroll
-        for (int h = 0; h < NH; ++h) load_cols<D>(o.kc[h], rk, k0, h, g, c);
+        for (int h = 0; h < NH; ++h) load_cols(o.kc[h], rk, k0, D, 64 * h, g, c);
     };
     auto compute = [&](int st, const Ops &cur) {
         const int k0 = st * kStep;
-        const f32x4 s = product<D>(cur.k, qv);   // s[r]: S[myq][k0 + 4g + r]
-        const f32x4 dp = product<D>(cur.v, gv);  // dP, same slots
+        const f32x4 s = product(cur.k, qv);   // s[r]: S[myq][k0 + 4g + r]
+        const f32x4 dp = product(cur.v, gv);  // dP, same slots
         const bool in_slice = st < st1;
         float ds[4];
 #pragma unroll
@@ -243,19 +245,26 @@ __global__ __launch_bounds__(kW * 64, 1) void bwd_f32_dq_kernel(
     }
 }
 
+// dK/dV.  At D = 128 the waves of a pair (2s, 2s + 1) walk the same queries:
+// wave h forms the part of S and dP that columns 64h..64h+63 contribute, the
+// pair adds its two parts through LDS, and each wave keeps dK and dV for its
+// own 64 columns.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kW * 64, 1) void bwd_f32_dkdv_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     const float *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
     float *__restrict__ dK, float *__restrict__ dV, int Nq, int Nk, float scale,
     float scale_log2) {
-    constexpr int CS = D / 64;   // waves per query slice, one per 64-column half
+    constexpr int CS = D / 64;   // waves per query slice, one per 64 columns
     constexpr int NS = kW / CS;  // query slices
     __shared__ __attribute__((aligned(16))) float s_acc[2][NS][kT][D];
+    // the pair's exchange of partial S and dP: [step parity][wave][S, dP][lane]
+    __shared__ __attribute__((aligned(16))) f32x4 s_part[CS == 2 ? 2 : 1][CS == 2 ? kW : 1][2][64];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slice = wave / CS, h = wave % CS;
+    const int col0 = 64 * h;
     const int g = lane >> 4, c = lane & 15;
     int kt, bh;
     tile_head((Nk + kT - 1) / kT, false, kt, bh);  // causal: the first keys see the most queries
@@ -269,9 +278,9 @@ __global__ __launch_bounds__(kW * 64, 1) void bwd_f32_dkdv_kernel(
     const auto rl = make_rsrc(LSE + (size_t)bh * Nq, (uint32_t)Nq * 4);
     const auto rd = make_rsrc(Delta + (size_t)bh * Nq, (uint32_t)Nq * 4);
 
-    float kq[D / 4], vq[D / 4];  // B operands: this lane's key row of K and of V
-    load_bop<D>(kq, rk, myk, g);
-    load_bop<D>(vq, rv, myk, g);
+    float kq[16], vq[16];  // B operands: this lane's key row of K and of V, this wave's columns
+    load_bop<4>(kq, rk, myk, D, col0, g);
+    load_bop<4>(vq, rv, myk, D, col0, g);
     const bool klive = myk < Nk;
 
     // Causal: queries before k0 see none of these keys.
@@ -280,29 +289,48 @@ __global__ __launch_bounds__(kW * 64, 1) void bwd_f32_dkdv_kernel(
     const int per = (nsteps + NS - 1) / NS;
     const int st0 = slice * per;
     const int st1 = min(nsteps, st0 + per);
+    // with the exchange every wave runs the same number of steps (each step
+    // has a barrier); past st1 they are masked
+    const int st_end = CS == 2 ? st0 + per : st1;
 
-    // [j][r] = dK (/ scale), dV of key myk, column 64h + 16g + 4r + j
+    // [j][r] = dK (/ scale), dV of key myk, column col0 + 16g + 4r + j
     f32x4 dk[4], dv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) dk[j] = dv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     struct Ops {
-        Op<D / 16> qr, gr;  // Q and dO by rows (first products)
-        Op<4> qc, gc;       // Q and dO by columns, this wave's 64-column block
-        f32x4 l, d;         // L and D of queries q0 + 4g .. + 3
+        Op<4> qr, gr;  // Q and dO by rows (first products), this wave's columns
+        Op<4> qc, gc;  // Q and dO by columns (second products), this wave's columns
+        f32x4 l, d;    // L and D of queries q0 + 4g .. + 3
     };
     auto load = [&](Ops &o, int q0) {
-        load_rows<D>(o.qr, rq, q0, g, c);
-        load_rows<D>(o.gr, rdo, q0, g, c);
-        load_cols<D>(o.qc, rq, q0, h, g, c);
-        load_cols<D>(o.gc, rdo, q0, h, g, c);
+        load_rows(o.qr, rq, q0, D, col0, g, c);
+        load_rows(o.gr, rdo, q0, D, col0, g, c);
+        load_cols(o.qc, rq, q0, D, col0, g, c);
+        load_cols(o.gc, rdo, q0, D, col0, g, c);
         o.l = __builtin_bit_cast(f32x4, load16(rl, (uint32_t)((q0 + 4 * g) * 4)));
         o.d = __builtin_bit_cast(f32x4, load16(rd, (uint32_t)((q0 + 4 * g) * 4)));
     };
-    auto compute = [&](int st, const Ops &cur) {
+    // One 16-query step on `cur`, with the next step's operands loaded into
+    // `nxt` first (in-range data or zeros), so that the loads overlap this
+    // step's products.
+    auto step = [&](int st, int parity, const Ops &cur, Ops &nxt) {
         const int q0 = qstart + st * kStep;
-        const f32x4 s = product<D>(cur.qr, kq);   // s[r]: S[q0 + 4g + r][myk]
-        const f32x4 dp = product<D>(cur.gr, vq);  // dP, same slots
+        load(nxt, q0 + kStep);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 s = product(cur.qr, kq);   // s[r]: S[q0 + 4g + r][myk]
+        f32x4 dp = product(cur.gr, vq);  // dP, same slots
+        if constexpr (CS == 2) {
+            // Both waves of the pair add the same two values (addition is
+            // commutative), so their P and dS agree bit for bit.  The parity
+            // keeps a fast wave's next write off the buffer its partner may
+            // still be reading: that write comes after the next barrier.
+            s_part[parity][wave][0][lane] = s;
+            s_part[parity][wave][1][lane] = dp;
+            __syncthreads();
+            s += s_part[parity][wave ^ 1][0][lane];
+            dp += s_part[parity][wave ^ 1][1][lane];
+        }
         const bool in_slice = st < st1;
         float p[4], ds[4];
 #pragma unroll
@@ -317,32 +345,18 @@ __global__ __launch_bounds__(kW * 64, 1) void bwd_f32_dkdv_kernel(
         accumulate(dk, cur.qc, ds);
     };
 
-    if constexpr (D == 64) {
-        auto step = [&](int st, const Ops &cur, Ops &nxt) {
-            load(nxt, qstart + (st + 1) * kStep);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(st, cur);
-        };
-        Ops ra, rb;
-        load(ra, qstart + st0 * kStep);
-        for (int st = st0; st < st1; st += 2) {
-            step(st, ra, rb);
-            step(st + 1, rb, ra);
-        }
-    } else {
-        // a second set of D = 128 operands does not fit the registers
-        Ops cur;
-        for (int st = st0; st < st1; ++st) {
-            load(cur, qstart + st * kStep);
-            compute(st, cur);
-        }
+    Ops ra, rb;
+    load(ra, qstart + st0 * kStep);
+    for (int st = st0; st < st_end; st += 2) {
+        step(st, 0, ra, rb);
+        step(st + 1, 1, rb, ra);
     }
 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<f32x4 *>(&s_acc[0][slice][c][64 * h + 16 * g + 4 * r]) =
+        *reinterpret_cast<f32x4 *>(&s_acc[0][slice][c][col0 + 16 * g + 4 * r]) =
             f32x4{dk[0][r], dk[1][r], dk[2][r], dk[3][r]};
-        *reinterpret_cast<f32x4 *>(&s_acc[1][slice][c][64 * h + 16 * g + 4 * r]) =
+        *reinterpret_cast<f32x4 *>(&s_acc[1][slice][c][col0 + 16 * g + 4 * r]) =
             f32x4{dv[0][r], dv[1][r], dv[2][r], dv[3][r]};
     }
     __syncthreads();
