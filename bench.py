@@ -120,6 +120,11 @@ def decode_inputs(cfg):
     return out
 
 
+def f32_peak(dtype):
+    """float32 workloads are rated against the float32 matrix-core peak."""
+    return {"peak_tflops": PEAK_F32} if dtype == "f32" else {}
+
+
 def extra_cases():
     """The workloads reported under ``extra``, one at a time, as (name, call,
     flops, info, calls per timing sample); each case's inputs are made when it
@@ -127,11 +132,11 @@ def extra_cases():
 
     Forward: the multi-head f16/bf16 shape (no LSE), the causal f16 workload
     (with LSE, causal and not), and the generalised prefill shapes (D = 128,
-    a ragged N = 2000, Nq != Nk).  Backward: attn_bwd alone on the multi-head
-    N = 2048 shape (f16, bf16, causal f16, and f16 at D = 128) and on the
-    single-head f32 N = 4096 shape (O and the LSE from one untimed attn_fwd),
-    10*Nq*Nk*D flops per head (five products), halved when causal; the f32
-    case is rated against the f32 peak."""
+    a ragged N = 2000, Nq != Nk; D = 128 also in f32).  Backward: attn_bwd
+    alone on the multi-head N = 2048 shape (f16, bf16, causal f16, and f16 and
+    f32 at D = 128) and on the single-head f32 N = 4096 shape (O and the LSE
+    from one untimed attn_fwd), 10*Nq*Nk*D flops per head (five products),
+    halved when causal.  f32 cases are rated against the f32 peak."""
     import dataclasses
 
     import torch
@@ -141,7 +146,7 @@ def extra_cases():
     fwd = [workloads.multihead(2048, "f16"), workloads.multihead(2048, "bf16"),
            workloads.causal_lse(True), workloads.causal_lse(False)]
     fwd += [workloads.Prefill("B4 H12 M=N=2048 D128 %s" % dt, 4, 12, 2048, 2048, 128, dt,
-                              1 / math.sqrt(128), False, 0) for dt in ("f16", "bf16")]
+                              1 / math.sqrt(128), False, 0) for dt in ("f16", "bf16", "f32")]
     fwd += [workloads.Prefill("B4 H12 M=N=2000 D64 f16 (ragged)", 4, 12, 2000, 2000, 64, "f16",
                               0.125, False, 0),
             workloads.Prefill("B4 H12 M=1024 N=4096 D64 f16", 4, 12, 1024, 4096, 64, "f16",
@@ -156,13 +161,13 @@ def extra_cases():
         assert need <= ws.numel()
         yield (cfg.name, lambda: fa2.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o,
                                               return_lse=with_lse, lse=lse, workspace=ws),
-               cfg.flops, {"lse": with_lse}, 50)
+               cfg.flops, dict({"lse": with_lse}, **f32_peak(cfg.dtype)), 50)
         del q, k, v, o, lse
     del ws
     bwd = [dataclasses.replace(workloads.multihead(2048, dt), causal=causal)
            for dt, causal in (("f16", False), ("bf16", False), ("f16", True))]
-    bwd.append(workloads.Prefill("B4 H12 M=N=2048 D128 f16", 4, 12, 2048, 2048, 128, "f16",
-                                 1 / math.sqrt(128), False, 0))
+    bwd += [workloads.Prefill("B4 H12 M=N=2048 D128 %s" % dt, 4, 12, 2048, 2048, 128, dt,
+                              1 / math.sqrt(128), False, 0) for dt in ("f16", "f32")]
     bwd.append(workloads.HEADLINE_F32)
     for cfg in bwd:
         dt, causal = cfg.dtype, cfg.causal
@@ -174,7 +179,7 @@ def extra_cases():
         yield ("bwd %s%s" % (cfg.name, " causal" if causal else ""),
                lambda: fa2.attn_bwd(q, k, v, o, g, lse, scale=cfg.scale, causal=causal, dq=dq_,
                                     dk=dk_, dv=dv_, delta=delta),
-               2.5 * cfg.flops, {"peak_tflops": PEAK_F32} if dt == "f32" else {}, 20)
+               2.5 * cfg.flops, f32_peak(dt), 20)
         del q, k, v, g, o, lse, dq_, dk_, dv_, delta
 
 

@@ -141,10 +141,9 @@ size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int causal, 
  *   formed in float32.  F32: float32 MFMA operands, nothing is rounded to a
  *   narrower type.  With Nq == 0, dk and dv are set to zero.  The results do
  *   not depend on timing (no atomics): equal inputs give equal bits.
- *   Supported: D == 64 or 128 with F16 or BF16, D == 64 with F32 (F32 with
- *   D == 128 -> FA2_ERR_UNSUPPORTED); any B, H, Nq >= 0 (B*H == 0 enqueues
- *   nothing); Nk >= 1; B*H*ceil(max(Nq,Nk) / W) < 2^24 with W = 128
- *   (D = 64) or 64 (D = 128).
+ *   Supported: D == 64 or 128 with F32, F16 or BF16; any B, H, Nq >= 0
+ *   (B*H == 0 enqueues nothing); Nk >= 1; B*H*ceil(max(Nq,Nk) / W) < 2^24
+ *   with W = 128 (D = 64) or 64 (D = 128).
  */
 fa2_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
                     const void *dout, const float *lse, void *dq, void *dk, void *dv,
