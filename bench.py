@@ -16,8 +16,9 @@ D64, no LSE) and the causal f16 workload (Z1 H2 N1024, scale 0.5, with LSE,
 causal and not) are timed as the FlashAttention-2 README times its table
 (warm-up, then the median of 7 samples of 50 back-to-back calls, HIP events)
 and reported under ``extra`` (not part of ``value``), as are the generalised
-prefill shapes (D = 128 in f16 and bf16, a ragged N = 2000, Nq != Nk) and the
-backward (attn_bwd) on the multi-head shape in f16 and bf16, and causal f16.
+prefill shapes (D = 128 in f16, bf16 and f32, a ragged N = 2000, Nq != Nk) and
+the backward (attn_bwd) on the multi-head shape in f16 and bf16, causal f16,
+f16 and f32 at D = 128, and on the single-head f32 shape.
 
 The fp64 CPU oracle is timed on the host cores first (``cpu_baseline``): the
 whole headline workload, all 4096 rows, repeated for about three seconds.
