@@ -126,13 +126,34 @@ def f32_peak(dtype):
     return {"peak_tflops": PEAK_F32} if dtype == "f32" else {}
 
 
+GRAPH_CALLS = 20
+
+
+def capture(fn, n):
+    """A HIP graph of n back-to-back calls of fn (torch.cuda.graph; one
+    warm-up call on a side stream first, as torch recommends)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(n):
+            fn()
+    torch.cuda.synchronize()
+    return graph
+
+
 def extra_cases():
     """The workloads reported under ``extra``, one at a time, as (name, call,
     flops, info, calls per timing sample); each case's inputs are made when it
     is reached and dropped after.
 
     Forward: the multi-head f16/bf16 shape (no LSE), the causal f16 workload
-    (with LSE, causal and not), and the generalised prefill shapes (D = 128,
+    (with LSE, causal and not; also replayed from a HIP graph of 20 calls,
+    "us" then per call), and the generalised prefill shapes (D = 128,
     a ragged N = 2000, Nq != Nk; D = 128 also in f32).  Backward: attn_bwd
     alone on the multi-head N = 2048 shape (f16, bf16, causal f16, and f16 and
     f32 at D = 128) and on the single-head f32 N = 4096 shape (O and the LSE
@@ -160,10 +181,17 @@ def extra_cases():
         need = fa2.workspace_size(cfg.B, cfg.H, cfg.Nq, cfg.Nk, cfg.D, cfg.causal,
                                   fa2.dtype_code(q))
         assert need <= ws.numel()
-        yield (cfg.name, lambda: fa2.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o,
-                                              return_lse=with_lse, lse=lse, workspace=ws),
-               cfg.flops, dict({"lse": with_lse}, **f32_peak(cfg.dtype)), 50)
-        del q, k, v, o, lse
+        call = lambda: fa2.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal,  # noqa: E731
+                                    out=o, return_lse=with_lse, lse=lse, workspace=ws)
+        yield cfg.name, call, cfg.flops, dict({"lse": with_lse}, **f32_peak(cfg.dtype)), 50
+        if with_lse:
+            # the same calls replayed from a HIP graph, as a serving loop would
+            # run this small, launch-bound shape (no host work per call)
+            graph = capture(call, GRAPH_CALLS)
+            yield (cfg.name + " (HIP graph of %d calls)" % GRAPH_CALLS, graph.replay,
+                   GRAPH_CALLS * cfg.flops, {"lse": True, "calls_per_replay": GRAPH_CALLS}, 5)
+            del graph
+        del q, k, v, o, lse, call
     del ws
     bwd = [dataclasses.replace(workloads.multihead(2048, dt), causal=causal)
            for dt, causal in (("f16", False), ("bf16", False), ("f16", True))]
@@ -275,6 +303,7 @@ def main():
             ms = time_median(call, calls=calls)
             tf = flops / (ms * 1e-3) / 1e12
             peak = info.get("peak_tflops", PEAK_F16)
+            ms /= info.get("calls_per_replay", 1)  # reported per call
             extra[name] = dict({"us": round(ms * 1e3, 2), "tflops": round(tf, 2),
                                 "frac_of_mfma_peak": round(tf / peak, 4)}, **info)
             log("%s: %.2f us, %.1f TFLOP/s (%.1f%% of MFMA peak)" % (name, ms * 1e3, tf,
