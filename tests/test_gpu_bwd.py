@@ -195,19 +195,21 @@ def test_bwd_deterministic(dt, D):
     assert all(torch.equal(x, y) for x, y in zip(a, b))
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dt", ["f16", "bf16", "f32"])
-def test_bwd_offsets_past_2_31_elements(dt):
-    """B*H = 8192 heads of N = 4096: each [B,H,N,64] tensor holds 2^31
-    elements (4 GiB), so the last heads sit past any 32-bit element offset.
+def test_bwd_offsets_past_2_31_elements(dt, D):
+    """B*H = 8192 heads of N = 4096 at D = 64 (4096 heads at D = 128): each
+    [B,H,N,D] tensor holds 2^31 elements, so the last heads sit past any
+    32-bit element offset.
     Q = K = 0 makes every P exactly 2^-12; with dO and V in {-1, +1} the
     gradients are exact: dQ = dK = 0 and dV_j = 2^-12 sum_q dO_q for every key
     j (a sum of 4096 terms of +-1, exact in float32).  Checked in full for the
     first, a middle and the last heads, and dQ = dK = 0 everywhere."""
     import torch
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dt]
-    B, H, N = 128, 64, 4096
+    B, H, N = 128 * 64 // D, 64, 4096
     gen = torch.Generator(device="cuda").manual_seed(7)
-    shape = (B, H, N, 64)
+    shape = (B, H, N, D)
     q = torch.zeros(shape, device="cuda", dtype=tdt)
     k = torch.zeros(shape, device="cuda", dtype=tdt)
     v = (torch.randint(0, 2, shape, device="cuda", generator=gen, dtype=torch.int8) * 2 - 1).to(tdt)
@@ -217,8 +219,8 @@ def test_bwd_offsets_past_2_31_elements(dt):
     torch.cuda.synchronize()
     assert torch.count_nonzero(dq).item() == 0
     assert torch.count_nonzero(dk).item() == 0
-    gf = g.view(B * H, N, 64)
-    dvf = dv.view(B * H, N, 64)
+    gf = g.view(B * H, N, D)
+    dvf = dv.view(B * H, N, D)
     for head in (0, B * H // 2 + 3, B * H - 1):
         # the exact value, rounded to the output dtype as the kernel rounds its exact f32 sum
         want = (gf[head].double().sum(dim=0) / N).to(tdt).double()

@@ -56,14 +56,15 @@ def test_decode_largest_slice(dt):
     _free(k, v, q, o)
 
 
-@pytest.mark.parametrize("dt", ["f16", "f32"])
-def test_forward_largest_slice(dt):
+@pytest.mark.parametrize("dt,D", [("f16", 64), ("f32", 64), ("f16", 128), ("bf16", 128),
+                                  ("f32", 128)])
+def test_forward_largest_slice(dt, D):
     import torch
-    dtype = torch.float16 if dt == "f16" else torch.float32
-    es = 2 if dt == "f16" else 4
-    D = 64
+    dtype = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dt]
+    es = 4 if dt == "f32" else 2
     Nk = MAX_SLICE // (D * es)
-    Nq = 100  # one ragged query tile: the keys are split across workgroups
+    Nq = 100  # one ragged query tile: the keys are split across workgroups (f32 at D = 128:
+    # seven 16-row workgroups whose waves each walk an eighth of the keys)
     k, v = _kv(Nk, D, dtype)
     g = torch.Generator(device="cuda").manual_seed(6)
     qrow = torch.randn((1, 1, 1, D), generator=g, device="cuda").to(dtype)
