@@ -1,5 +1,5 @@
-"""Parity on a fixed list of pseudo-random shapes, forward and backward,
-against the fp64 oracle through the C ABI.
+"""Parity on a fixed list of pseudo-random shapes, forward, backward and
+flash-decoding, against the fp64 oracle through the C ABI.
 
 The named workloads and the hand-picked ragged cases test what was designed
 for; this list (drawn once from a seeded generator, so every run checks the
@@ -94,10 +94,27 @@ def _large_backward_cases(n=12, seed=11):
     return out
 
 
+def _decode_cases(n=48, seed=777):
+    """Flash-decoding: lengths log-uniform on [1, 70000], split counts from 1
+    to 64 (more splits than 64-key blocks included), unusual scales."""
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = ("f16", "bf16", "f32")[i % 3]
+        D = int(g.choice([64, 128]))
+        B, H = int(g.integers(1, 5)), int(g.integers(1, 9))
+        N = int(min(70000, max(1, round(math.exp(g.uniform(0, math.log(70000)))))))
+        ns = int(g.choice([1, 2, 3, 5, 8, 13, 16, 32, 64]))
+        scale = float(g.choice([D ** -0.5, D ** -0.5, 0.0, -0.1, 0.5]))
+        out.append((B, H, N, D, dt, ns, scale, 300 + i))
+    return out
+
+
 FWD = _forward_cases()
 BWD = _backward_cases()
 FWD_LARGE = _large_forward_cases()
 BWD_LARGE = _large_backward_cases()
+DEC = _decode_cases()
 
 
 def _id(c):
@@ -190,3 +207,22 @@ def test_decode_unusual_scales(scale, dt):
     q64, k64, v64 = (inputs.to_f64(x, dt) for x in (q, k, v))
     ref = oracle.attn(q64[:, :, None], k64, v64, scale)[0][:, :, 0]
     assert_close("decode scale %g %s" % (scale, dt), o, ref, edge_tol(dt, ref, o))
+
+
+@pytest.mark.parametrize("case", DEC, ids=lambda c: "B%dH%d_N%d_D%d_%s_ns%d_s%.3g" % c[:7])
+def test_decode(case):
+    """The combined output against the oracle's attention of the one row, and
+    the partials against the oracle's split."""
+    import oracle
+    from exact_attention_fa2_amd import inputs
+    from gpu_util import TOL, assert_close, edge_tol
+    from test_gpu_decode import check_partials
+    from test_gpu_decode import run as run_decode
+    B, H, N, D, dt, ns, scale, seed = case
+    name = "random decode B%d H%d N%d D%d %s splits %d scale %g" % (B, H, N, D, dt, ns, scale)
+    (q, k, v, sc), o, op, mp, lp = run_decode(B, H, N, D, dt, ns, seed=seed, scale=scale)
+    q64, k64, v64 = (inputs.to_f64(x, dt) for x in (q, k, v))
+    ro = oracle.attn(q64[:, :, None], k64, v64, sc)[0][:, :, 0]
+    assert_close(name, o, ro, edge_tol(dt, ro, o))
+    rop, rmp, rlp = oracle.decode_split(q64, k64, v64, sc, ns)
+    check_partials(name + " partials", op, mp, lp, rop, rmp, rlp, TOL[dt])
