@@ -232,27 +232,41 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
                 f32x4{acc[4 * h][r], acc[4 * h + 1][r], acc[4 * h + 2][r], acc[4 * h + 3][r]};
     __syncthreads();
 
-    // Merge the wave states of each row: one output element per thread and
-    // pass (one pass at D = 64, four at D = 128).
-    for (int e = threadIdx.x; e < kQT * D; e += W * 64) {
-        const int row = e / D;
-        const int d = e % D;
+    // Merge the wave states of each row ((m, l) merge of the online softmax).
+    // First one thread per row: the row's max m and denominator l, its LSE,
+    // the weight 2^(m_w - m) of every wave's unnormalised O, and 1 / l.  The
+    // row's s_m entries, read only by this thread, then hold the weights and
+    // s_l[0][row] holds 1 / l, so no more LDS is needed.
+    if (threadIdx.x < kQT) {
+        const int row = threadIdx.x;
         float mg = -INFINITY;
 #pragma unroll
         for (int w = 0; w < W; ++w) mg = fmaxf(mg, s_m[w][row]);
-        float lg = 0.f, o0 = 0.f;
+        float wt[W];
+        float lg = 0.f;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
             const float mw = s_m[w][row];
-            const float wt = mw == -INFINITY ? 0.f : exp2f_fast(mw - mg);
-            lg += wt * s_l[w][row];
-            o0 += wt * s_o[w][row][d];
+            wt[w] = mw == -INFINITY ? 0.f : exp2f_fast(mw - mg);
+            lg += wt[w] * s_l[w][row];
         }
+#pragma unroll
+        for (int w = 0; w < W; ++w) s_m[w][row] = wt[w];
+        s_l[0][row] = 1.f / lg;
         const int qrow = q0 + row;
-        if (qrow < Nq) {
-            O[((size_t)bh * Nq + qrow) * D + d] = o0 / lg;
-            if (LSE && d == 0) LSE[(size_t)bh * Nq + qrow] = (mg + log2f_fast(lg)) * kLn2;
-        }
+        if (LSE && qrow < Nq) LSE[(size_t)bh * Nq + qrow] = (mg + log2f_fast(lg)) * kLn2;
+    }
+    __syncthreads();
+    // Then one output element per thread and pass (one pass at D = 64, four
+    // at D = 128): the weighted sum of the waves' O, divided by l once.
+    for (int e = threadIdx.x; e < kQT * D; e += W * 64) {
+        const int row = e / D;
+        const int d = e % D;
+        float o0 = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) o0 = __builtin_fmaf(s_m[w][row], s_o[w][row][d], o0);
+        const int qrow = q0 + row;
+        if (qrow < Nq) O[((size_t)bh * Nq + qrow) * D + d] = o0 * s_l[0][row];
     }
 }
 
