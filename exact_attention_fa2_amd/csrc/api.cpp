@@ -48,6 +48,12 @@ bool valid_dtype(int dt) { return dt == FA2_F32 || dt == FA2_F16 || dt == FA2_BF
 
 namespace {
 
+size_t fwd_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, fa2_dtype dtype,
+                           int cus) {
+    if (dtype == FA2_F32) return fa2::f32_workspace_bytes(B, H, Nq, Nk, D, cus);
+    return fa2::mfma_workspace_bytes(B, H, Nq, Nk, D, causal, cus);
+}
+
 fa2_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                     int Nq, int Nk, int D, float scale, int causal, fa2_dtype dtype,
                     void *workspace, size_t workspace_bytes, void *stream) {
@@ -99,8 +105,7 @@ FA2_API size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int 
     if ((long long)B * H > 65535) return 0;
     int cus = 256;
     if (const DeviceInfo *dev = current_device()) cus = dev->num_cus;
-    if (dtype == FA2_F32) return fa2::f32_workspace_bytes(B, H, Nq, Nk, D, cus);
-    return fa2::mfma_workspace_bytes(B, H, Nq, Nk, D, causal, cus);
+    return fwd_workspace_bytes(B, H, Nq, Nk, D, causal, dtype, cus);
 }
 
 FA2_API fa2_status attn_bwd(const void *q, const void *k, const void *v, const void *o,

@@ -82,6 +82,19 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _alloc(stream, *args, like=None, **kw):
+    """A tensor the binding allocates for a call on ``stream``.  torch's
+    caching allocator ties a new tensor to the current stream; when the
+    kernels run on another stream, the tensor is also recorded on that one,
+    so its memory is not handed out again before the kernels are done with
+    it (this matters for the ones dropped at the end of the call)."""
+    torch = _torch()
+    t = torch.empty_like(like) if like is not None else torch.empty(*args, **kw)
+    if stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+    return t
+
+
 def _check(fn, status):
     if status != 0:
         raise FA2Error(fn, status)
@@ -143,9 +156,9 @@ def attn_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc(stream, like=q)
     if return_lse and lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+        lse = _alloc(stream, (B, H, Nq), dtype=torch.float32, device=q.device)
     if not use_workspace:
         st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
                             _ptr(lse if return_lse else None), B, H, Nq, Nk, D, float(scale),
@@ -156,7 +169,7 @@ def attn_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=
     if need and workspace is not None:
         _validate(q, [(workspace, "workspace", None, None)])
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _alloc(stream, need, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace) if need else None
     ws_bytes = workspace.numel() * workspace.element_size() if need else 0
     st = lib().attn_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse if return_lse else None),
@@ -185,11 +198,11 @@ def attn_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, 
     dc = dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = _alloc(stream, like=q) if dq is None else dq
+    dk = _alloc(stream, like=k) if dk is None else dk
+    dv = _alloc(stream, like=v) if dv is None else dv
     if delta is None:
-        delta = torch.empty((B, H, Nq), dtype=f32, device=q.device)
+        delta = _alloc(stream, (B, H, Nq), dtype=f32, device=q.device)
     st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                         _ptr(dk), _ptr(dv), _ptr(delta), B, H, Nq, Nk, D, float(scale),
                         int(bool(causal)), dc, _stream(stream))
@@ -215,11 +228,11 @@ def attn_decode_split(q, k, v, scale, n_splits, o_part=None, m_part=None, l_part
     _validate(q, specs)
     dc = dtype_code(q)
     if o_part is None:
-        o_part = torch.empty((B, H, n_splits, D), dtype=torch.float32, device=q.device)
+        o_part = _alloc(stream, (B, H, n_splits, D), dtype=torch.float32, device=q.device)
     if m_part is None:
-        m_part = torch.empty((B, H, n_splits), dtype=torch.float32, device=q.device)
+        m_part = _alloc(stream, (B, H, n_splits), dtype=torch.float32, device=q.device)
     if l_part is None:
-        l_part = torch.empty((B, H, n_splits), dtype=torch.float32, device=q.device)
+        l_part = _alloc(stream, (B, H, n_splits), dtype=torch.float32, device=q.device)
     st = lib().attn_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(m_part),
                                  _ptr(l_part), B, H, N, D, float(scale), n_splits, dc,
                                  _stream(stream))
@@ -238,7 +251,7 @@ def attn_decode_combine(o_part, m_part, l_part, dtype, out=None, stream=None):
         specs.append((out, "out", (B, H, D), dtype))
     _validate(o_part, specs)
     if out is None:
-        out = torch.empty((B, H, D), dtype=dtype, device=o_part.device)
+        out = _alloc(stream, (B, H, D), dtype=dtype, device=o_part.device)
     st = lib().attn_decode_combine(_ptr(o_part), _ptr(m_part), _ptr(l_part), _ptr(out), B, H,
                                    D, S, dtype_code(out), _stream(stream))
     _check("attn_decode_combine", st)

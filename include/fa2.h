@@ -21,7 +21,11 @@
  *   Errors     Arguments are checked before anything is enqueued; a rejected
  *              call enqueues nothing.  A failed launch is reported as
  *              FA2_ERR_LAUNCH.  The library never aborts the process.
- *   Limits     One (b,h) slice of k or v must be smaller than 2 GiB.
+ *   Limits     One (b,h) slice of q, k or v must be smaller than 2 GiB, and
+ *              B*H must be at most 65535 (attn_fwd, attn_fwd_ws, attn_bwd,
+ *              attn_decode_split); attn_bwd also needs
+ *              B*H*ceil(max(Nq,Nk) / W) < 2^24 with W = 128 (D = 64) or 64
+ *              (D = 128).  Requests beyond these return FA2_ERR_UNSUPPORTED.
  */
 #ifndef FA2_H
 #define FA2_H
@@ -43,7 +47,8 @@ typedef enum {
     FA2_ERR_NULL = 1,        /* a required pointer is NULL */
     FA2_ERR_SHAPE = 2,       /* a size is negative or zero where it must be positive */
     FA2_ERR_UNSUPPORTED = 3, /* valid request this build does not implement (D, dtype,
-                                causal with Nq != Nk, slice >= 2 GiB) */
+                                causal with Nq != Nk, a non-finite scale, a slice of
+                                2 GiB or more, B*H > 65535, the backward's grid limit) */
     FA2_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     FA2_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch */
     FA2_ERR_DEVICE = 6       /* no usable gfx950 device, or a device query failed */
@@ -75,9 +80,9 @@ typedef enum {
  *   both products on MFMA with P rounded to the input dtype; float32 inputs
  *   run both products on float32 MFMA (no reduced-precision rounding).
  *   o is rounded to nearest-even into dtype.
- *   Supported: D == 64 or 128 with dtype F32, F16 or BF16; any B, H,
- *   Nq >= 0 (zero-size outputs enqueue nothing); Nk >= 1; ragged Nq/Nk are
- *   masked in the tail.
+ *   Supported: D == 64 or 128 with dtype F32, F16 or BF16; B, H >= 0 with
+ *   B*H <= 65535; Nq >= 0 (zero-size outputs enqueue nothing); Nk >= 1;
+ *   ragged Nq/Nk are masked in the tail.
  */
 fa2_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                     int B, int H, int Nq, int Nk, int D, float scale, int causal,
@@ -141,9 +146,9 @@ size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int causal, 
  *   formed in float32.  F32: float32 MFMA operands, nothing is rounded to a
  *   narrower type.  With Nq == 0, dk and dv are set to zero.  The results do
  *   not depend on timing (no atomics): equal inputs give equal bits.
- *   Supported: D == 64 or 128 with F32, F16 or BF16; any B, H, Nq >= 0
- *   (B*H == 0 enqueues nothing); Nk >= 1; B*H*ceil(max(Nq,Nk) / W) < 2^24
- *   with W = 128 (D = 64) or 64 (D = 128).
+ *   Supported: D == 64 or 128 with F32, F16 or BF16; B, H >= 0 with
+ *   B*H <= 65535, Nq >= 0 (B*H == 0 enqueues nothing); Nk >= 1;
+ *   B*H*ceil(max(Nq,Nk) / W) < 2^24 with W = 128 (D = 64) or 64 (D = 128).
  */
 fa2_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
                     const void *dout, const float *lse, void *dq, void *dk, void *dv,
@@ -166,8 +171,8 @@ fa2_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
  *   q [B,H,D] dtype;  k, v [B,H,N,D] dtype
  *   o_part [B,H,n_splits,D] float32;  m_part, l_part [B,H,n_splits] float32
  *   Supported: D in {64, 128}; dtype F16, BF16, F32; N >= 1; n_splits >= 1;
- *   any finite scale (otherwise FA2_ERR_UNSUPPORTED); B*H == 0 enqueues
- *   nothing.
+ *   B*H <= 65535; any finite scale (otherwise FA2_ERR_UNSUPPORTED); B*H == 0
+ *   enqueues nothing.
  */
 fa2_status attn_decode_split(const void *q, const void *k, const void *v,
                              float *o_part, float *m_part, float *l_part,

@@ -68,6 +68,11 @@ def test_fwd_error_paths():
     assert L.attn_fwd(ok, ok, ok, ok, ctypes.c_void_p(4098), 1, 1, 4, 4, 64, 0.1, 0, 1, None) == 4
     # a slice of 2 GiB or more is refused up front
     assert _fwd(Nk=1 << 24, D=64) == 3
+    # B*H is limited to 65535 (the grids' second dimension)
+    assert _fwd(B=256, H=256) == 3
+    assert _fwd(B=1, H=65536) == 3
+    assert fa2.lib().attn_fwd_ws(*([ctypes.c_void_p(4096)] * 4), None, 2, 32768, 4, 4, 64, 0.1, 0, 1,
+                                 None, 0, None) == 3
 
 
 def test_fwd_empty_outputs_enqueue_nothing():
@@ -94,6 +99,7 @@ def test_decode_error_paths():
     assert split(q=None) == 1
     assert split(q=ctypes.c_void_p(4100)) == 4
     assert split(B=0) == 0
+    assert split(B=256, H=256) == 3
     assert L.attn_decode_combine(ok, ok, ok, ok, 1, 1, 128, 0, 1, None) == 2
     assert L.attn_decode_combine(ok, ok, ok, None, 1, 1, 128, 4, 1, None) == 1
     assert L.attn_decode_combine(ok, ok, ok, ok, 1, 1, 80, 4, 1, None) == 3
@@ -168,6 +174,9 @@ def test_bwd_error_paths():
         assert L.attn_bwd(*ptrs, 1, 1, 4, 4, 64, 0.1, 0, 1, None) == 4, pos
     assert _bwd(Nk=1 << 24) == 3
     assert _bwd(B=300, H=300) == 3
+    assert _bwd(B=256, H=256) == 3
+    # the grid limit: B*H*ceil(max(Nq,Nk)/128) must stay below 2^24 at D = 64
+    assert _bwd(B=1, H=65535, Nq=1 << 16, Nk=4) == 3
     # B*H == 0: a valid no-op, even with NULL pointers
     assert fa2.lib().attn_bwd(*([None] * 10), 0, 4, 4, 4, 64, 0.1, 0, 1, None) == 0
 

@@ -64,3 +64,57 @@ def test_decode_outputs():
     with pytest.raises(ValueError, match="out must have shape"):
         fa2.attn_decode_combine(o_part, m, m, torch.float16,
                                 out=torch.empty(2, 4, 64, device="cuda", dtype=torch.float16))
+
+
+def test_side_stream_buffers_are_not_reused_early(monkeypatch):
+    """Calls on a side stream while that stream is still busy: the workspace
+    of a split-path forward and the partials of attn_decode, which the binding
+    allocates and drops inside the call, must not be handed out again to an
+    allocation on the default stream before the side stream's kernels have
+    run; the results still match the oracle after a synchronisation."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from exact_attention_fa2_amd import inputs
+    from gpu_util import TOL, assert_close, download_f64, upload
+
+    made = []
+    real = fa2._alloc
+
+    def spy(*a, **kw):
+        t = real(*a, **kw)
+        made.append((t.data_ptr(), t.numel() * t.element_size()))
+        return t
+    monkeypatch.setattr(fa2, "_alloc", spy)
+
+    q, k, v = inputs.qkv((1, 2, 1024, 64), (1, 2, 1024, 64), 21, "f16")
+    tq, tk, tv = upload(q, "f16"), upload(k, "f16"), upload(v, "f16")
+    need = fa2.workspace_size(1, 2, 1024, 1024, 64, True, fa2.FA2_F16)
+    assert need > 0, "this shape is meant to split its keys"
+    qd = inputs.normal((2, 4, 128), 22, 0, "f16")
+    kd = inputs.normal((2, 4, 3000, 128), 22, 1, "f16")
+    vd = inputs.normal((2, 4, 3000, 128), 22, 2, "f16")
+    tqd, tkd, tvd = upload(qd, "f16"), upload(kd, "f16"), upload(vd, "f16")
+    torch.cuda.synchronize()
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(50_000_000)  # keep the side stream busy while the host goes on
+    o, lse = fa2.attn_fwd(tq, tk, tv, scale=0.5, causal=True, return_lse=True, stream=s)
+    od = fa2.attn_decode(tqd, tkd, tvd, n_splits=6, stream=s)
+    grabbed = [torch.empty(n, dtype=torch.uint8, device="cuda") for _, n in made]
+    for g in grabbed:
+        g.fill_(0xFF)
+    for p, n in made:
+        for g in grabbed:
+            a = g.data_ptr()
+            assert a + g.numel() <= p or p + n <= a, \
+                "a buffer still in use on the side stream was handed out again"
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn(*(inputs.to_f64(x, "f16") for x in (q, k, v)), 0.5, True)
+    assert_close("side stream O", download_f64(o), ro, TOL["f16"])
+    assert_close("side stream LSE", download_f64(lse), rl, 1e-4)
+    rd, _ = oracle.attn(inputs.to_f64(qd, "f16")[:, :, None], inputs.to_f64(kd, "f16"),
+                        inputs.to_f64(vd, "f16"), 1 / np.sqrt(128))
+    assert_close("side stream decode", download_f64(od), rd[:, :, 0], TOL["f16"])

@@ -70,14 +70,10 @@ def test_multihead_full(n, dt):
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
-def test_multihead_2048_sampled(dt):
-    cfg = workloads.multihead(2048, dt)
-    g = np.random.default_rng(1)
-    total = cfg.B * cfg.H * cfg.Nq
-    # every row of the first and last head plus 1024 random rows
-    rows = np.unique(np.concatenate([np.arange(cfg.Nq), np.arange(total - cfg.Nq, total),
-                                     g.choice(total, 1024, replace=False)]))
-    check_full(cfg, rows)
+def test_multihead_2048_full(dt):
+    """The multi-head workload at its primary length, every one of the
+    4*12*2048 rows (O and LSE) against the oracle, at the plain bar."""
+    check_full(workloads.multihead(2048, dt))
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
@@ -201,13 +197,11 @@ def test_large_score_shift_is_safe(dt):
                        0.5)[0]
     assert np.max(np.abs(rl)) > 100
     assert np.all(np.isfinite(o))
-    # Each score is now a float32 sum whose terms reach ~100, so it carries an
-    # absolute rounding error of a few ulp(128) = 1.5e-5; the softmax weights
-    # inherit that as a relative error, which can exceed the 1e-4 f32 bar on
-    # O.  Half-precision inputs keep their own (looser) bar.
-    tol = 5e-4 if dt == "f32" else edge_tol(dt, ro, o, wabs)
+    # float32 keeps the plain 1e-4 bar even with scores near 100 (measured
+    # 3.7e-5); half-precision inputs keep their own bound.
+    tol = TOL["f32"] if dt == "f32" else edge_tol(dt, ro, o, wabs)
     assert_close("shift O " + dt, o, ro, tol)
-    assert_close("shift LSE " + dt, lse, rl, 1e-4 * max(1.0, float(np.max(np.abs(rl)))))
+    assert_close("shift LSE " + dt, lse, rl, LSE_TOL)
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
