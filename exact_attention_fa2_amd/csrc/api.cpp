@@ -17,15 +17,27 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr long long kMaxSliceBytes = (1LL << 31) - (1LL << 20);
 
+// Workspace of attn_fwd_noalloc: the key-split partials of the forward live
+// in this array instead of caller or library allocations.  Every device the
+// library is loaded on holds its own copy, from the moment the code object is
+// loaded until the process ends; all attn_fwd_noalloc calls on one device
+// share it.  Host code never uses the name itself as an address (on the host
+// it is only a handle): each device's address is looked up once, below.
+constexpr size_t kScratchBytes = FA2_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 struct DeviceInfo {
     int ok = 0;
     int num_cus = 0;
+    void *scratch = nullptr;  // this device's copy of `scratch` (null if the lookup failed)
 };
 
 std::once_flag g_once[kMaxDevices];
 DeviceInfo g_info[kMaxDevices];
 
-// Properties of the current device, filled once per device (thread-safe).
+// Properties of the current device, filled once per device (thread-safe),
+// with that device current: its compute units, whether it is a gfx950, and
+// the device address of its scratch array.
 const DeviceInfo *current_device() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
@@ -34,6 +46,13 @@ const DeviceInfo *current_device() {
         if (hipGetDeviceProperties(&p, dev) != hipSuccess) return;
         g_info[dev].num_cus = p.multiProcessorCount;
         g_info[dev].ok = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+        if (g_info[dev].ok) {
+            void *ptr = nullptr;
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess)
+                g_info[dev].scratch = ptr;
+            else
+                (void)hipGetLastError();  // leave no sticky error for the caller's next call
+        }
     });
     return g_info[dev].ok ? &g_info[dev] : nullptr;
 }
@@ -54,9 +73,12 @@ size_t fwd_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, fa2_
     return fa2::mfma_workspace_bytes(B, H, Nq, Nk, D, causal, cus);
 }
 
+// use_scratch: take the device's scratch array as the workspace (shapes that
+// would need more are refused).
 fa2_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                     int Nq, int Nk, int D, float scale, int causal, fa2_dtype dtype,
-                    void *workspace, size_t workspace_bytes, void *stream) {
+                    void *workspace, size_t workspace_bytes, void *stream,
+                    bool use_scratch = false) {
     if (B < 0 || H < 0 || Nq < 0 || Nk < 1 || D < 1) return FA2_ERR_SHAPE;
     if (!valid_dtype(dtype)) return FA2_ERR_UNSUPPORTED;
     if (causal != 0 && causal != 1) return FA2_ERR_UNSUPPORTED;
@@ -74,6 +96,13 @@ fa2_status fwd_impl(const void *q, const void *k, const void *v, void *o, float 
     if ((long long)B * H > 65535) return FA2_ERR_UNSUPPORTED;
     const DeviceInfo *dev = current_device();
     if (!dev) return FA2_ERR_DEVICE;
+    if (use_scratch) {
+        if (fwd_workspace_bytes(B, H, Nq, Nk, D, causal, dtype, dev->num_cus) > kScratchBytes)
+            return FA2_ERR_UNSUPPORTED;
+        if (!dev->scratch) return FA2_ERR_DEVICE;
+        workspace = dev->scratch;
+        workspace_bytes = kScratchBytes;
+    }
     fa2::FwdArgs a{q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dev->num_cus,
                    workspace, workspace ? workspace_bytes : 0};
     hipStream_t st = (hipStream_t)stream;
@@ -95,6 +124,13 @@ FA2_API fa2_status attn_fwd_ws(const void *q, const void *k, const void *v, void
                                void *stream) {
     return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, workspace,
                     workspace_bytes, stream);
+}
+
+FA2_API fa2_status attn_fwd_noalloc(const void *q, const void *k, const void *v, void *o,
+                                    float *lse, int B, int H, int Nq, int Nk, int D, float scale,
+                                    int causal, fa2_dtype dtype, void *stream) {
+    return fwd_impl(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, dtype, nullptr, 0, stream,
+                    true);
 }
 
 FA2_API size_t attn_fwd_workspace_size(int B, int H, int Nq, int Nk, int D, int causal,

@@ -18,8 +18,10 @@ STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "unsupported config
           4: "pointer not 16-byte aligned", 5: "kernel launch failed",
           6: "no usable gfx950 device"}
 
-EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "attn_bwd", "attn_decode_split",
-           "attn_decode_combine", "attn_decode_default_splits", "fa2_status_string")
+EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_noalloc", "attn_fwd_workspace_size", "attn_bwd",
+           "attn_decode_split", "attn_decode_combine", "attn_decode_default_splits",
+           "fa2_status_string")
+NOALLOC_SCRATCH_BYTES = 32 << 20  # FA2_NOALLOC_SCRATCH_BYTES in include/fa2.h
 
 _lib = None
 
@@ -43,6 +45,8 @@ def lib():
         L.attn_fwd.restype = i
         L.attn_fwd_ws.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
         L.attn_fwd_ws.restype = i
+        L.attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp]
+        L.attn_fwd_noalloc.restype = i
         L.attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
         L.attn_fwd_workspace_size.restype = ctypes.c_size_t
         L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, fp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp]
@@ -177,6 +181,28 @@ def attn_fwd(q, k, v, scale=None, causal=False, return_lse=False, out=None, lse=
                            _stream(stream))
     _check("attn_fwd", st)
     return (out, lse) if return_lse else out
+
+
+def attn_fwd_noalloc(q, k, v, out, scale=None, causal=False, lse=None, stream=None):
+    """attn_fwd through the entry point that allocates nothing (its key-split
+    workspace is the library's own device array).  The caller passes ``out``
+    [B,H,Nq,D] and, to get the LSE, ``lse`` [B,H,Nq] float32; nothing is
+    allocated here either.  Calls that overlap in time on one device race on
+    that array.  Returns ``out`` (and ``lse`` when given)."""
+    torch = _torch()
+    B, H, Nq, D = _dims(q, 4, "q")
+    Nk = _dims(k, 4, "k")[2]
+    specs = [(q, "q", None, None), (k, "k", (B, H, Nk, D), q.dtype), (v, "v", (B, H, Nk, D), q.dtype),
+             (out, "out", q.shape, q.dtype)]
+    if lse is not None:
+        specs.append((lse, "lse", (B, H, Nq), torch.float32))
+    _validate(q, specs)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = lib().attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, D,
+                                float(scale), int(bool(causal)), dtype_code(q), _stream(stream))
+    _check("attn_fwd_noalloc", st)
+    return out if lse is None else (out, lse)
 
 
 def attn_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None,

@@ -110,6 +110,32 @@ fa2_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, flo
                        fa2_dtype dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * attn_fwd_noalloc -- attn_fwd_ws for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Nothing is allocated or freed by the call.
+ *
+ * Same arguments and result as attn_fwd (the caller passes the inputs and
+ * the outputs o and lse); the workspace that attn_fwd_ws would take from the
+ * caller is the library's own device array of FA2_NOALLOC_SCRATCH_BYTES
+ * bytes, one per device, which every device the library is loaded on holds
+ * until the process ends.
+ *   Errors   A shape whose workspace (attn_fwd_workspace_size) exceeds
+ *            FA2_NOALLOC_SCRATCH_BYTES returns FA2_ERR_UNSUPPORTED (on a
+ *            256-CU MI355X only a few head-dimension-128 shapes with few
+ *            query tiles); use attn_fwd_ws for those.  FA2_ERR_DEVICE if the
+ *            array's device address cannot be obtained.
+ *   Races    All attn_fwd_noalloc calls on one device share its array, which
+ *            keeps the last call's contents: calls that can overlap in time on
+ *            one device (different streams, or different host threads) race.
+ *            Serialise them, e.g. issue them on one stream.  The array's
+ *            contents on entry are never read before they are written.
+ */
+#define FA2_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+fa2_status attn_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                            fa2_dtype dtype, void *stream);
+
+/*
  * attn_fwd_workspace_size -- bytes of workspace attn_fwd_ws would use for
  * this shape on the current device (0: it would not split, or the shape is
  * not supported).  If the device cannot be queried it assumes 256 compute
