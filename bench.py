@@ -8,8 +8,11 @@ HBM:
     32 heads, one query row, KV length 32768, D = 128, float16.
 ``value`` is the forward's TFLOP/s (4*Nq*Nk*D flops over its mean time per
 step); the decode's KV GB/s rides along in ``decode``.  Both carry a roofline
-fraction; the kernels' own durations come from HIP events recorded on the
-stream the kernels are launched on, around each part of every timed step.
+fraction; the kernels' own durations come from HIP events on the stream the
+kernels are launched on: each kernel of every timed step records a pair of
+events from its own dispatch (fa2.time_next_launch, hipExtLaunchKernel), so
+the interval is that kernel alone, and ``ms_per_step`` comes from events
+around all the timed steps.
 
 Order of a run (so that no idle gap precedes any timing):
   1. CPU leg: the fp64 oracle is timed on the headline workload on the host
@@ -385,6 +388,12 @@ def main():
                     help="only run the extra workloads whose name contains PATTERN, "
                          "--profile-calls times each (for counter profiles), and exit")
     ap.add_argument("--profile-calls", type=int, default=5)
+    ap.add_argument("--extra-only", default=None, metavar="PATTERN",
+                    help="only time the extra workloads whose name contains PATTERN (same "
+                         "protocol), print them as one JSON line, and exit")
+    ap.add_argument("--library", default=None, metavar="PATH",
+                    help="use this build of the library instead of libfa2.so (for example "
+                         "exact_attention_fa2_amd/libfa2_polyexp.so)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (to scale the FETCH_SIZE "
                          "and WRITE_SIZE counters of a profile) and exit")
@@ -405,7 +414,27 @@ def main():
         print(json.dumps({"copy_bytes": 1 << 30, "calls": 5}))
         return
 
-    from exact_attention_fa2_amd import workloads
+    import torch  # noqa: F401  (before any library load: one HIP runtime in the process)
+
+    from exact_attention_fa2_amd import fa2 as _fa2, workloads
+    if args.library:
+        _fa2._lib = _fa2.load(os.path.abspath(args.library))
+    if args.extra_only is not None:
+        import torch
+        torch.cuda.set_device(0)
+        cases = build_extras({}, {}, {}, args.extra_only)
+        med = time_extras(cases)
+        out = {}
+        for c in cases:
+            ms = med[c.name]
+            rate = c.work / (ms * 1e-3) / (1e12 if c.unit == "TFLOP/s" else 1e9)
+            out[c.name] = {"us": round(ms * 1e3, 2), "rate": round(rate, 2), "unit": c.unit,
+                           "frac_of_peak": round(rate / c.peak, 4)}
+            log("%s: %.2f us, %.1f %s (%.1f%% of peak)" % (c.name, ms * 1e3, rate, c.unit,
+                                                           100 * rate / c.peak))
+        print(json.dumps({"library": os.path.basename(args.library or _fa2.LIB_PATH),
+                          "extra": out}), flush=True)
+        return
     pre = workloads.HEADLINE_F32
     dec = workloads.decode(args.decode_dtype)
     want_extra = not args.no_extra and args.profile_extra is None
@@ -520,27 +549,32 @@ def main():
         pw_ms += s.elapsed_time(e)
         pw_steps += n
 
+    # Each kernel of a timed step records a pair of events from its own
+    # dispatch (fa2.time_next_launch), so its interval is the kernel alone;
+    # the step's own events bracket all K steps.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    for row in ev:
+        for e in row:
+            e.record()  # created before the timed region
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(K):
-        ev[i][0].record()
+        fa2.time_next_launch(ev[i][0], ev[i][1])
         prefill()
-        ev[i][1].record()
+        fa2.time_next_launch(ev[i][2], ev[i][3])
         split()
-        ev[i][2].record()
+        fa2.time_next_launch(ev[i][4], ev[i][5])
         combine()
-        ev[i][3].record()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     pre_t = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    split_t = [e[1].elapsed_time(e[2]) for e in ev]
-    comb_t = [e[2].elapsed_time(e[3]) for e in ev]
+    split_t = [e[2].elapsed_time(e[3]) for e in ev]
+    comb_t = [e[4].elapsed_time(e[5]) for e in ev]
     dec_t = sorted(a + b for a, b in zip(split_t, comb_t))
     pre_ms = sum(pre_t) / K
     split_ms = sum(split_t) / K

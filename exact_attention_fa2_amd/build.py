@@ -22,6 +22,13 @@ OUT = os.path.join(PKG, "libfa2.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "fwd_f32.hip", "fwd_mfma.hip", "decode.hip", "bwd.hip", "bwd_f32.hip"]
+# Measurement builds beside the product library: (file name, source rebuilt
+# with extra flags, flags); the other objects are shared with libfa2.so.
+VARIANTS = [
+    # 2 of every 8 exponential pairs of the f16/bf16 forward on the FMA path
+    # (polynomial exp2), to time that lever in the kernel and check its parity
+    ("libfa2_polyexp.so", "fwd_mfma.hip", ["-DFA2_POLY_EXP=2"]),
+]
 ARCH = "gfx950"
 
 COMMON = [
@@ -44,9 +51,9 @@ def build(asm_dir: str | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     hipcc = _hipcc()
 
-    def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc, "-c", os.path.join(CSRC, src), "-o", obj] + COMMON
+    def compile_one(src, tag="", extra=()):
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + tag + ".o")
+        cmd = [hipcc, "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + list(extra)
         if src.endswith(".cpp"):
             cmd += ["-x", "hip"]
         if asm_dir and src.endswith(".hip"):
@@ -61,14 +68,23 @@ def build(asm_dir: str | None = None, verbose: bool = False) -> str:
             print(msg, file=sys.stderr)
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = [hipcc, "-shared", "-o", tmp] + objs + ["--offload-arch=" + ARCH, "-fPIC"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, OUT)
+    jobs = [(src, "", ()) for src in SOURCES]
+    jobs += [(src, "." + name, tuple(flags)) for name, src, flags in VARIANTS]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: compile_one(*j), jobs))
+    base = objs[:len(SOURCES)]
+
+    def link(out, objects):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [hipcc, "-shared", "-o", tmp] + objects + ["--offload-arch=" + ARCH, "-fPIC"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+        os.replace(tmp, out)
+
+    link(OUT, base)
+    for (name, src, _), obj in zip(VARIANTS, objs[len(SOURCES):]):
+        link(os.path.join(PKG, name), [obj if s == src else o for s, o in zip(SOURCES, base)])
     return OUT
 
 

@@ -227,6 +227,13 @@ FA2_API int attn_decode_default_splits(int B, int H, int N, int D) {
     return (int)want;
 }
 
+FA2_API fa2_status fa2_time_next_launch(void *start_event, void *stop_event) {
+    fa2::TimingRequest &tr = fa2::timing_request();
+    tr.start = (hipEvent_t)start_event;
+    tr.stop = (hipEvent_t)stop_event;
+    return FA2_OK;
+}
+
 FA2_API const char *fa2_status_string(fa2_status s) {
     switch (s) {
         case FA2_OK: return "ok";

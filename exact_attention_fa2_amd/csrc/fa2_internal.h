@@ -1,17 +1,38 @@
 // fa2_internal.h -- launchers shared between the kernel sources and the C ABI.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include "../../include/fa2.h"
 
 namespace fa2 {
 
-// Launch a kernel with hipLaunchKernel so the runtime's verdict is returned.
+// The calling thread's pending request from fa2_time_next_launch: the next
+// launch records these events from its own dispatch, then clears them.
+struct TimingRequest {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+inline TimingRequest &timing_request() {
+    static thread_local TimingRequest r;
+    return r;
+}
+
+// Launch a kernel so that the runtime's verdict is returned: hipLaunchKernel,
+// or hipExtLaunchKernel with the thread's pending timing events (the events
+// then carry the kernel's own start and end).
 template <typename... KArgs, typename... Args>
 inline fa2_status launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
                          Args... args) {
     static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
     void *ptrs[] = {(void *)&args...};
-    hipError_t e = hipLaunchKernel((const void *)kern, grid, block, ptrs, 0, st);
+    TimingRequest &tr = timing_request();
+    hipError_t e;
+    if (tr.start || tr.stop) {
+        const TimingRequest use = tr;
+        tr = TimingRequest{};
+        e = hipExtLaunchKernel((const void *)kern, grid, block, ptrs, 0, st, use.start, use.stop, 0);
+    } else {
+        e = hipLaunchKernel((const void *)kern, grid, block, ptrs, 0, st);
+    }
     return e == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 

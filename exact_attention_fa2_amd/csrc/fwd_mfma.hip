@@ -105,6 +105,32 @@ __device__ __forceinline__ int vswz(int key) {
     return FA2_VSWZ ? j ^ ((j & 1) << 2) : key & 7;
 }
 
+// FA2_POLY_EXP = k (0..8): in every 32-key tile, k of each group's 8 pairs of
+// exponentials are computed by exp2_poly on the FMA path instead of by
+// v_exp_f32 -- the FlashAttention-4 lever of running a polynomial exponential
+// beside the hardware one ("Flash Attention", section FlashAttention 4).  The
+// pairs are spread evenly over the tile.  On gfx950 both run on the same
+// vector ALU (v_exp_f32 costs about three FMA issue slots), so the product
+// build uses 0; a build with k > 0 exists to measure that in the kernel.
+#ifndef FA2_POLY_EXP
+#define FA2_POLY_EXP 0
+#endif
+
+// 2^x = 2^n 2^f with n = floor(x), f = x - n in [0, 1) (exact in f32), and
+// 2^f from a cubic whose coefficients were fitted here to the least maximum
+// relative error on [0, 1) (8.6e-5 in f32 arithmetic, below the half-ulp of
+// the f16 and bf16 P it feeds).  x is clamped at -128, where the result is
+// 2^-128: zero once P is rounded to f16, and below 1e-38 in bf16.
+__device__ __forceinline__ float exp2_poly(float x) {
+    x = fmaxf(x, -128.f);
+    const float n = __builtin_floorf(x);
+    const float f = x - n;
+    const float p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(0.07706704f, f, 0.22764499f), f,
+                                                  0.69511676f),
+                                   f, 1.f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
 // max over the two lanes l and l^32 of a wave (v_permlane32_swap exchanges the
 // halves of a register pair; either output pairing gives both halves).
 __device__ __forceinline__ float max_halves(float x) {
@@ -366,8 +392,11 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 8 * c + 2 * j;
-                    const float p0 = exp2f_fast(__builtin_fmaf(scur[g][r], scale_log2, -m_use));
-                    const float p1 = exp2f_fast(__builtin_fmaf(scur[g][r + 1], scale_log2, -m_use));
+                    const float x0 = __builtin_fmaf(scur[g][r], scale_log2, -m_use);
+                    const float x1 = __builtin_fmaf(scur[g][r + 1], scale_log2, -m_use);
+                    const bool poly = FA2_POLY_EXP > 0 && ((4 * c + j) * FA2_POLY_EXP) % 8 < FA2_POLY_EXP;
+                    const float p0 = poly ? exp2_poly(x0) : exp2f_fast(x0);
+                    const float p1 = poly ? exp2_poly(x1) : exp2f_fast(x1);
                     const uint32_t w = pack2<DT>(p0, p1);
                     pk[g][c][j] = w;
                     if constexpr (WLSE) ps[g][j & 1] += p0 + p1;

@@ -12,6 +12,7 @@ import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa2.so")
+POLYEXP_LIB_PATH = os.path.join(_PKG, "libfa2_polyexp.so")  # measurement build (polynomial exp2)
 
 FA2_F32, FA2_F16, FA2_BF16 = 0, 1, 2
 STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "unsupported configuration",
@@ -20,7 +21,7 @@ STATUS = {0: "ok", 1: "null pointer", 2: "invalid shape", 3: "unsupported config
 
 EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_noalloc", "attn_fwd_workspace_size", "attn_bwd",
            "attn_decode_split", "attn_decode_combine", "attn_decode_default_splits",
-           "fa2_status_string")
+           "fa2_time_next_launch", "fa2_status_string")
 NOALLOC_SCRATCH_BYTES = 32 << 20  # FA2_NOALLOC_SCRATCH_BYTES in include/fa2.h
 
 _lib = None
@@ -36,31 +37,46 @@ def lib():
     """Load libfa2.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError("libfa2.so is not built (%s); run "
-                               "`python -m exact_attention_fa2_amd.build`" % LIB_PATH)
-        L = ctypes.CDLL(LIB_PATH)
-        vp, fp, i, f = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-        L.attn_fwd.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp]
-        L.attn_fwd.restype = i
-        L.attn_fwd_ws.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
-        L.attn_fwd_ws.restype = i
-        L.attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp]
-        L.attn_fwd_noalloc.restype = i
-        L.attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
-        L.attn_fwd_workspace_size.restype = ctypes.c_size_t
-        L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, fp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp]
-        L.attn_bwd.restype = i
-        L.attn_decode_split.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, f, i, i, vp]
-        L.attn_decode_split.restype = i
-        L.attn_decode_combine.argtypes = [fp, fp, fp, vp, i, i, i, i, i, vp]
-        L.attn_decode_combine.restype = i
-        L.attn_decode_default_splits.argtypes = [i, i, i, i]
-        L.attn_decode_default_splits.restype = i
-        L.fa2_status_string.argtypes = [i]
-        L.fa2_status_string.restype = ctypes.c_char_p
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
+
+
+def load(path):
+    """A ctypes handle on one build of the library (libfa2.so, or a
+    measurement build beside it such as libfa2_polyexp.so), with the
+    signatures of include/fa2.h.  Raises if it has not been built."""
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built (%s); run `python -m exact_attention_fa2_amd.build`"
+                           % (os.path.basename(path), path))
+    # torch first: it brings its own HIP runtime and asks for it by another
+    # file name than the library does, so a library loaded before torch would
+    # pull in the system runtime as a second copy, whose device state the
+    # tensors' runtime does not share (hipGetDevice then reports no device).
+    # Loaded after torch, the library binds to torch's runtime by its soname.
+    _torch()
+    L = ctypes.CDLL(path)
+    vp, fp, i, f = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp]
+    L.attn_fwd.restype = i
+    L.attn_fwd_ws.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp, ctypes.c_size_t, vp]
+    L.attn_fwd_ws.restype = i
+    L.attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp]
+    L.attn_fwd_noalloc.restype = i
+    L.attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    L.attn_fwd_workspace_size.restype = ctypes.c_size_t
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, fp, vp, vp, vp, fp, i, i, i, i, i, f, i, i, vp]
+    L.attn_bwd.restype = i
+    L.attn_decode_split.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, f, i, i, vp]
+    L.attn_decode_split.restype = i
+    L.attn_decode_combine.argtypes = [fp, fp, fp, vp, i, i, i, i, i, vp]
+    L.attn_decode_combine.restype = i
+    L.attn_decode_default_splits.argtypes = [i, i, i, i]
+    L.attn_decode_default_splits.restype = i
+    L.fa2_time_next_launch.argtypes = [vp, vp]
+    L.fa2_time_next_launch.restype = i
+    L.fa2_status_string.argtypes = [i]
+    L.fa2_status_string.restype = ctypes.c_char_p
+    return L
 
 
 def _torch():
@@ -298,6 +314,20 @@ def attn_decode(q, k, v, scale=None, n_splits=None, stream=None):
         n_splits = default_splits(B, H, N, D)
     parts = attn_decode_split(q, k, v, scale, n_splits, stream=stream)
     return attn_decode_combine(*parts, dtype=q.dtype, stream=stream)
+
+
+def time_next_launch(start, stop):
+    """The next kernel this thread enqueues through the library records the
+    torch.cuda.Event ``start`` and ``stop`` (enable_timing=True) from its own
+    dispatch: ``start.elapsed_time(stop)`` is then that kernel's execution
+    alone.  Either may be None."""
+    def handle(ev):
+        if ev is None:
+            return None
+        if not ev.cuda_event:  # torch creates the event on its first record
+            ev.record()
+        return ctypes.c_void_p(ev.cuda_event)
+    _check("fa2_time_next_launch", lib().fa2_time_next_launch(handle(start), handle(stop)))
 
 
 def status_string(code: int) -> str:

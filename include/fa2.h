@@ -12,9 +12,10 @@
  *              device properties.
  *   Launch     Work is enqueued on `stream` and the call returns at once.
  *              Results are valid after the stream is synchronised.  Calls on
- *              one stream run in order; the library keeps no state between
- *              calls, so calls on different streams may overlap when their
- *              output buffers do not.
+ *              one stream run in order; apart from a pending timing request
+ *              (fa2_time_next_launch, per host thread) the library keeps no
+ *              state between calls, so calls on different streams may overlap
+ *              when their output buffers do not (attn_fwd_noalloc aside).
  *   Layouts    Contiguous row-major, innermost dimension last.  Element type
  *              of q/k/v/o is `dtype`; lse and decode partials are float32.
  *   Alignment  Every pointer must be 16-byte aligned (128-bit loads/stores).
@@ -231,6 +232,20 @@ fa2_status attn_decode_combine(const float *o_part, const float *m_part, const f
  * >= 1; if the device cannot be queried it assumes 256 compute units.
  */
 int attn_decode_default_splits(int B, int H, int N, int D);
+
+/*
+ * fa2_time_next_launch -- measurement aid: the next kernel that the calling
+ * host thread enqueues through this library (through any entry point)
+ * records `start_event` when it starts and `stop_event` when it ends, from
+ * the kernel's own dispatch (hipExtLaunchKernel), so that their elapsed time
+ * is that kernel's execution alone, without the queue's gap before it or the
+ * marker packets of separately recorded events.  Both are hipEvent_t handles
+ * created with timing enabled, or NULL (NULL, NULL cancels a pending
+ * request).  The request is used by exactly one launch: an entry point that
+ * enqueues several kernels (a key-split forward and its combine, the
+ * backward's three passes) times the first.  Never fails (FA2_OK).
+ */
+fa2_status fa2_time_next_launch(void *start_event, void *stop_event);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *fa2_status_string(fa2_status s);

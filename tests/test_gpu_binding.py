@@ -118,3 +118,52 @@ def test_side_stream_buffers_are_not_reused_early(monkeypatch):
     rd, _ = oracle.attn(inputs.to_f64(qd, "f16")[:, :, None], inputs.to_f64(kd, "f16"),
                         inputs.to_f64(vd, "f16"), 1 / np.sqrt(128))
     assert_close("side stream decode", download_f64(od), rd[:, :, 0], TOL["f16"])
+
+
+def test_time_next_launch_times_one_kernel():
+    """fa2.time_next_launch: the next launch records the two events from its
+    own dispatch; the interval is positive and no longer than events recorded
+    around the same call, and the request is used by that one launch only."""
+    import torch
+    q = torch.randn(1, 1, 4096, 64, device="cuda")
+    f = lambda: fa2.attn_fwd(q, q, q, scale=0.125)  # noqa: E731
+    f()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    a, b, outer0, outer1 = E(), E(), E(), E()
+    outer0.record()
+    fa2.time_next_launch(a, b)
+    f()
+    outer1.record()
+    torch.cuda.synchronize()
+    inner, outer = a.elapsed_time(b), outer0.elapsed_time(outer1)
+    assert 0 < inner <= outer, (inner, outer)
+    # consumed: a second call leaves the events as they were
+    f()
+    torch.cuda.synchronize()
+    assert a.elapsed_time(b) == inner
+    fa2.time_next_launch(None, None)  # cancelling is allowed
+
+
+def test_library_loaded_before_torch_is_imported():
+    """A process that loads the library before it imports torch: the binding
+    imports torch first, so the library binds to torch's HIP runtime and sees
+    the device its tensors live on (a second runtime would report none).  Run
+    in a fresh interpreter, since this one has imported torch already."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from exact_attention_fa2_amd import fa2\n"
+        "fa2.lib()\n"
+        "import torch\n"
+        "q = torch.randn(1, 2, 300, 64, device='cuda', dtype=torch.float16)\n"
+        "o = fa2.attn_fwd(q, q, q, scale=0.125)\n"
+        "r = torch.softmax(q.float() @ q.float().transpose(-1, -2) * 0.125, -1) @ q.float()\n"
+        "torch.cuda.synchronize()\n"
+        "err = (o.float() - r).abs().max().item()\n"
+        "assert err < 4e-3, err\n"
+        "print('ok', err)\n" % root)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
