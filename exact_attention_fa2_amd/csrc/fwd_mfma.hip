@@ -595,8 +595,295 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Few query rows: one workgroup per 32 query rows whose W waves each walk a
+// contiguous slice of the keys, then merge their W partial states through LDS
+// with the (m, l) monoid ("Flash Attention", section Deriving the online
+// softmax: any grouping of the keys gives the same result).  This is the
+// key split of "Flash decoding" done inside one workgroup, so a shape with
+// too few query tiles to fill the device needs neither a workspace for
+// partials nor a second launch to combine them.
+//
+// Per wave and 32-key tile the arithmetic is that of fwd_mfma_kernel (S^T =
+// K Q^T with the next tile's scores issued during this tile's exponentials,
+// conditional rescaling, P rounded to the input dtype, O^T += V^T P^T).  K
+// goes straight from global memory into the MFMA A-operand registers (16
+// contiguous bytes per lane); V goes through the wave's own LDS double buffer
+// (a DMA per tile, swizzled as in fwd_mfma_kernel) for the transposed read;
+// K of tile t+2 and V of tile t+1 are in flight while tile t is computed.
+// After the walk the same LDS holds each wave's unnormalised O (32 x D floats).
+template <int D, int DT, bool CAUSAL, bool WLSE, int W>
+__global__ __launch_bounds__(W * 64, 1) void fwd_rows_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE, int Nq,
+    int Nk, float scale_log2, int n_qtiles) {
+    static_assert(D == 64, "head dimension");
+    constexpr int kD = D;
+    constexpr int NC = D / 16;            // 16-wide contraction chunks of S^T = K Q^T
+    constexpr int NT = D / 32;            // 32-column tiles of O^T
+    constexpr int CPR = D / 8;            // 16-byte chunks per row
+    constexpr int UPW = 32 * CPR / 64;    // 16-byte DMA units per lane per V tile
+    constexpr int TILE = 32 * D;          // 16-bit elements of one V tile
+    __shared__ __attribute__((aligned(16))) uint16_t sV[W * 2 * TILE];
+    __shared__ float s_m[W][32], s_lt[W][32], s_l[W][32];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5;
+    const int ql = lane & 31;
+
+    // b*h varies fastest; causal: the longest tiles first
+    const int n_bh = gridDim.x / n_qtiles;
+    int qt = blockIdx.x / n_bh;
+    const int bh = blockIdx.x - qt * n_bh;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;
+    const int q0 = qt * 32;
+
+    const uint16_t *Qh = Q + (size_t)bh * Nq * kD;
+    const uint16_t *Kh = K + (size_t)bh * Nk * kD;
+    const uint16_t *Vh = V + (size_t)bh * Nk * kD;
+    const auto rq = make_rsrc(Qh, (uint32_t)Nq * kD * 2);
+    const auto rk = make_rsrc(Kh, (uint32_t)Nk * kD * 2);
+    const auto rv = make_rsrc(Vh, (uint32_t)Nk * kD * 2);
+
+    // a negative scale goes onto Q, a zero scale is Q = 0 with scale 1 (as in
+    // fwd_mfma_kernel: maxima and masks are taken on unscaled scores)
+    const uint32_t qflip = scale_log2 < 0.f ? 0x80008000u : 0u;
+    const uint32_t qkeep = scale_log2 == 0.f ? 0u : 0xFFFFFFFFu;
+    scale_log2 = scale_log2 == 0.f ? 1.f : fabsf(scale_log2);
+
+    // B operand of S^T = K Q^T: chunk dc, slot (h, j) is Q[q0 + ql][16dc + 8h + j]
+    u32x4 qf[NC];
+#pragma unroll
+    for (int dc = 0; dc < NC; ++dc)
+        qf[dc] = (load16(rq, (uint32_t)(((q0 + ql) * kD + 16 * dc + 8 * h) * 2)) ^ qflip) & qkeep;
+
+    // this wave's 32-key tiles [t0, t1)
+    const int kend = CAUSAL ? min(Nk, q0 + 32) : Nk;
+    const int ntiles = (kend + 31) / 32;
+    const int per = (ntiles + W - 1) / W;
+    const int t0 = min(ntiles, wave * per);
+    const int t1 = min(ntiles, t0 + per);
+    uint16_t *vbuf = sV + wave * 2 * TILE;
+
+    // A operand of S^T = K Q^T for tile t: row ql is key 32t + ql, chunk dc
+    // holds its columns 16dc + 8h .. + 8 (zeros past Nk)
+    auto load_k = [&](int t, u32x4 (&kr)[NC]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int dc = 0; dc < NC; ++dc)
+            kr[dc] = load16(rk, (uint32_t)(((32 * t + ql) * kD + 16 * dc + 8 * h) * 2));
+    };
+    // V tile t -> LDS buffer t % 2: unit u of the tile holds chunk (u % CPR) ^
+    // vswz(row) of row u / CPR (rows past Nk load zeros)
+    auto dma_v = [&](int t) __attribute__((always_inline)) {
+        uint16_t *dst = vbuf + (t & 1) * TILE;
+#pragma unroll
+        for (int i = 0; i < UPW; ++i) {
+            const int unit = i * 64 + lane;
+            const int row = unit / CPR;
+            const int ch = (unit % CPR) ^ vswz<D>(row);
+            const uint32_t off = (uint32_t)(((32 * t + row) * kD + ch * 8) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dst + i * 512), 16, off, 0, 0, 0);
+        }
+    };
+    int vofs[NT][2];
+    {
+        const int i = lane & 15;
+        const int kl = 4 * h + (i >> 2);
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) {
+            const int d = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int key = kl + 8 * u;
+                vofs[dt][u] = key * kD + (((d >> 3) ^ vswz<D>(key)) << 3) + (d & 7);
+            }
+        }
+    }
+
+    float m = -INFINITY, l = 0.f, lt = 0.f;
+    const uint32_t ones = DT == 1 ? 0x3C003C00u : 0x3F803F80u;
+    f32x16 oacc[NT];
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+
+    // Tile t: scur holds S^T of tile t, kn the K operand of tile t+1 (NEXT);
+    // kld receives that of tile t+2.
+    auto tile = [&](const int t, const u32x4 (&kn)[NC], u32x4 (&kld)[NC], f32x16 &scur,
+                    f32x16 &snext, auto next_tag) __attribute__((always_inline)) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+        // V of tile t has landed, K of tile t+1 is in registers, and every LDS
+        // read of tile t-1 is done (its buffer takes tile t+1's V next)
+        __builtin_amdgcn_s_waitcnt(0);
+        if (t + 2 < t1) load_k(t + 2, kld);
+        if constexpr (NEXT) dma_v(t + 1);
+        const uint16_t *vt = vbuf + (t & 1) * TILE;
+        u32x4 vf[2][NT];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int dt = 0; dt < NT; ++dt) {
+                const uint16_t *src = vt + 16 * c * kD;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + vofs[dt][0]));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(src + vofs[dt][1]));
+                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+                const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+                vf[c][dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+            }
+        const int k0 = 32 * t;
+        if ((k0 + 32 > Nk) || (CAUSAL && k0 + 31 > q0)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                bool ok = key < Nk;
+                if (CAUSAL) ok = ok && key <= q0 + ql;
+                if (!ok) scur[r] = -INFINITY;
+            }
+        }
+        u32x4 pk[2];
+        float ps[2], lp[2];
+        auto exps = [&](float m_use, bool with_next) __attribute__((always_inline)) {
+            ps[0] = ps[1] = lp[0] = lp[1] = 0.f;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 8 * c + 2 * j;
+                    const float p0 = exp2f_fast(__builtin_fmaf(scur[r], scale_log2, -m_use));
+                    const float p1 = exp2f_fast(__builtin_fmaf(scur[r + 1], scale_log2, -m_use));
+                    const uint32_t w = pack2<DT>(p0, p1);
+                    pk[c][j] = w;
+                    if constexpr (WLSE) ps[j & 1] += p0 + p1;
+                    lp[j & 1] = dot2<DT>(w, ones, lp[j & 1]);
+                    if constexpr (NEXT) {
+                        if (with_next && c == 0)
+                            snext = MfmaT<DT>::mma(kn[j], qf[j], j == 0 ? f32x16{} : snext);
+                    }
+                }
+        };
+        // conditional rescaling, as in fwd_mfma_kernel
+        exps(m == -INFINITY ? 0.f : m, true);
+        if (__builtin_amdgcn_ballot_w64(m == -INFINITY || lp[0] + lp[1] > kLazyCap) != 0) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[r]);
+            mx = max_halves(mx) * scale_log2;
+            const float m_new = fmaxf(m, mx);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float corr = exp2f_fast(m - m_use);
+            l *= corr;
+            lt *= corr;
+#pragma unroll
+            for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[dt][i] *= corr;
+            m = m_new;
+            exps(m_use, false);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int dt = 0; dt < NT; ++dt) oacc[dt] = MfmaT<DT>::mma(vf[c][dt], pk[c], oacc[dt]);
+        lt += lp[0] + lp[1];
+        if constexpr (WLSE) l += ps[0] + ps[1];
+    };
+    auto run_tile = [&](const int t, const u32x4 (&kn)[NC], u32x4 (&kld)[NC], f32x16 &scur,
+                        f32x16 &snext) __attribute__((always_inline)) {
+        if (t + 1 < t1)
+            tile(t, kn, kld, scur, snext, std::true_type{});
+        else
+            tile(t, kn, kld, scur, snext, std::false_type{});
+    };
+
+    if (t0 < t1) {  // (wave-uniform)
+        u32x4 ka[NC], kb[NC];
+        load_k(t0, ka);
+        dma_v(t0);
+        load_k(t0 + 1, kb);  // (in-range rows or zeros when t0 + 1 >= t1; then unused)
+        f32x16 sa, sb;
+#pragma unroll
+        for (int dc = 0; dc < NC; ++dc) sa = MfmaT<DT>::mma(ka[dc], qf[dc], dc == 0 ? f32x16{} : sa);
+        for (int t = t0; t < t1; t += 2) {
+            run_tile(t, kb, ka, sa, sb);
+            if (t + 1 < t1) run_tile(t + 1, ka, kb, sb, sa);
+        }
+    }
+
+    // Merge.  oacc[dt][r] = O[q0 + ql][32dt + 8(r/4) + 4h + r%4] (unnormalised,
+    // base-2 max m); each lane holds half of the row's sums.
+    lt += __shfl_xor(lt, 32);
+    if constexpr (WLSE) l += __shfl_xor(l, 32);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // every wave is done with its V buffers
+    float *so = reinterpret_cast<float *>(sV) + wave * 32 * kD;
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int r = 4 * g4;
+            *reinterpret_cast<f32x4 *>(so + ql * kD + ((32 * dt + 8 * g4 + 4 * h) ^ (4 * (ql & 7)))) =
+                f32x4{oacc[dt][r], oacc[dt][r + 1], oacc[dt][r + 2], oacc[dt][r + 3]};
+        }
+    if (h == 0) {
+        s_m[wave][ql] = m;
+        s_lt[wave][ql] = lt;
+        s_l[wave][ql] = l;
+    }
+    __syncthreads();
+    // one thread per row: the row's max, each wave's weight 2^(m_w - m) (into
+    // s_m), 1 / sum of the rounded-P denominators (into s_lt[0]) and the LSE
+    if (threadIdx.x < 32) {
+        const int row = threadIdx.x;
+        float mg = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) mg = fmaxf(mg, s_m[w][row]);
+        float ltg = 0.f, lg = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float mw = s_m[w][row];
+            const float a = mw == -INFINITY ? 0.f : exp2f_fast(mw - mg);
+            s_m[w][row] = a;
+            ltg += a * s_lt[w][row];
+            if constexpr (WLSE) lg += a * s_l[w][row];
+        }
+        s_lt[0][row] = 1.f / ltg;
+        if constexpr (WLSE) {
+            if (q0 + row < Nq) LSE[(size_t)bh * Nq + q0 + row] = (mg + log2f_fast(lg)) * kLn2;
+        }
+    }
+    __syncthreads();
+    // four consecutive output columns per thread and pass
+    const float *sall = reinterpret_cast<const float *>(sV);
+    for (int e = 4 * (int)threadIdx.x; e < 32 * kD; e += 4 * W * 64) {
+        const int row = e / kD, col = e % kD;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(sall + (w * 32 + row) * kD +
+                                                             (col ^ (4 * (row & 7))));
+            acc += s_m[w][row] * v;
+        }
+        const float inv = s_lt[0][row];
+        if (q0 + row < Nq) {
+            u32x2 out;
+            out[0] = pack2<DT>(acc[0] * inv, acc[1] * inv);
+            out[1] = pack2<DT>(acc[2] * inv, acc[3] * inv);
+            *reinterpret_cast<u32x2 *>(O + ((size_t)bh * Nq + q0 + row) * kD + col) = out;
+        }
+    }
+}
+
+// Waves of fwd_rows_kernel (two per SIMD), each on its own slice of the keys.
+// The kernel runs at D = 64: at D = 128 its ring of operands does not fit two
+// waves' registers, and the key split across workgroups measured faster there.
+constexpr int kRowsWaves = 8;
+
 struct Plan {
     int qg, n_qtiles, n_tiles, chunks;
+    bool rows;  // few query tiles: fwd_rows_kernel (32-row workgroups, keys split across waves)
 };
 
 #ifndef FA2_MFMA_SPLIT_WGS
@@ -610,6 +897,13 @@ struct Plan {
 #endif
 #ifndef FA2_MFMA_SNAKE
 #define FA2_MFMA_SNAKE 1  // causal tiles in one round: deal them to CUs in a snake by length
+#endif
+#ifndef FA2_MFMA_ROWS
+#define FA2_MFMA_ROWS 1  // few query tiles: one launch of fwd_rows_kernel instead of split + combine
+#endif
+#ifndef FA2_MFMA_ROWS_MAX_NK
+#define FA2_MFMA_ROWS_MAX_NK 2048  // ... only when the keys are at most this long (with longer
+                                   // keys the key split across workgroups measured faster)
 #endif
 #ifndef FA2_MFMA_SPLIT_LONG
 #define FA2_MFMA_SPLIT_LONG 32  // also split when the tiles fill at most a quarter of the slots
@@ -632,8 +926,13 @@ Plan plan(int B, int H, int Nq, int Nk, int D, int num_cus) {
     const long long nt = (long long)p.n_qtiles * B * H;
     p.n_tiles = nt > 0x7FFFFFFF ? -1 : (int)nt;
     p.chunks = 1;
+    p.rows = false;
     const long long nblk = (Nk + kBC - 1) / kBC;
-    if (nt > 0 && nt * FA2_MFMA_SPLIT_BELOW <= num_cus) {
+    const long long nt32 = (long long)((Nq + 31) / 32) * B * H;
+    if (FA2_MFMA_ROWS && D == 64 && nt > 0 && nt * FA2_MFMA_SPLIT_BELOW <= num_cus &&
+        Nk <= FA2_MFMA_ROWS_MAX_NK && nt32 <= 0x7FFFFFFF) {
+        p.rows = true;
+    } else if (nt > 0 && nt * FA2_MFMA_SPLIT_BELOW <= num_cus) {
         long long c = ((long long)FA2_MFMA_SPLIT_WGS * num_cus + nt - 1) / nt;
         c = std::min<long long>(c, std::max<long long>(1, nblk / 2));
         p.chunks = (int)std::min<long long>(c, 32);
@@ -692,7 +991,20 @@ fa2_status launch_q(const FwdArgs &a, const Plan &p, hipStream_t st) {
 }
 
 template <int D, int DT, bool CAUSAL, bool WLSE>
+fa2_status launch_rows(const FwdArgs &a, hipStream_t st) {
+    const int n_qtiles = (a.Nq + 31) / 32;
+    const long long grid = (long long)n_qtiles * a.B * a.H;
+    return launch(fwd_rows_kernel<D, DT, CAUSAL, WLSE, kRowsWaves>, dim3((unsigned)grid),
+                  dim3(kRowsWaves * 64), st, (const uint16_t *)a.q, (const uint16_t *)a.k,
+                  (const uint16_t *)a.v, (uint16_t *)a.o, a.lse, a.Nq, a.Nk, a.scale * kLog2e,
+                  n_qtiles);
+}
+
+template <int D, int DT, bool CAUSAL, bool WLSE>
 fa2_status launch_v(const FwdArgs &a, const Plan &p, hipStream_t st) {
+    if constexpr (D == 64) {
+        if (p.rows) return launch_rows<D, DT, CAUSAL, WLSE>(a, st);
+    }
     if constexpr (FA2_MFMA_QG2 != 0 && D == 64) {
         if (p.qg == 2) return launch_q<D, DT, CAUSAL, WLSE, 2>(a, p, st);
     }
@@ -718,7 +1030,7 @@ fa2_status launch_fwd_mfma(const FwdArgs &a, fa2_dtype dt, hipStream_t st) {
 size_t mfma_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, int num_cus) {
     (void)causal;
     const Plan p = plan(B, H, Nq, Nk, D, num_cus);
-    if (p.chunks <= 1) return 0;
+    if (p.rows || p.chunks <= 1) return 0;
     return (size_t)B * H * Nq * p.chunks * (D + 3) * sizeof(float);
 }
 

@@ -124,15 +124,24 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 def test_workspace_size_plan():
     """attn_fwd_workspace_size without a GPU (256 compute units assumed)."""
     f16, bf16, f32 = fa2.FA2_F16, fa2.FA2_BF16, fa2.FA2_F32
-    # few query tiles: the keys are split, partials need (D + 3) floats per row and chunk
-    need = fa2.workspace_size(1, 2, 1024, 1024, 64, 1, f16)
-    assert need > 0 and need % (2 * 1024 * 67 * 4) == 0
-    assert fa2.workspace_size(1, 2, 1024, 1024, 64, 0, bf16) == need
+    # very few query tiles and keys up to 2048 at D = 64: one launch of 32-row
+    # workgroups whose waves split the keys, no workspace
+    assert fa2.workspace_size(1, 2, 1024, 1024, 64, 1, f16) == 0
+    assert fa2.workspace_size(1, 3, 129, 2000, 64, 0, bf16) == 0
+    # ... longer keys, or D = 128: the key split across workgroups
+    assert fa2.workspace_size(1, 1, 64, 4096, 64, 0, f16) > 0
+    assert fa2.workspace_size(1, 2, 1024, 1024, 128, 1, bf16) % (2 * 1024 * 131 * 4) == 0
+    assert fa2.workspace_size(1, 2, 1024, 1024, 128, 1, bf16) > 0
+    # long keys with the tiles filling at most a quarter of the workgroup
+    # slots: the keys are split, partials need (D + 3) floats per row and chunk
+    need = fa2.workspace_size(1, 4, 4096, 4096, 64, 1, f16)
+    assert need > 0 and need % (4 * 4096 * 67 * 4) == 0
+    assert fa2.workspace_size(1, 4, 4096, 4096, 64, 0, bf16) == need
     # enough query tiles to fill the device: no split
     assert fa2.workspace_size(4, 12, 2048, 2048, 64, 0, f16) == 0
     # D = 128 splits the same way, with D + 3 floats per row and chunk
-    need128 = fa2.workspace_size(1, 2, 1024, 1024, 128, 1, f16)
-    assert need128 > 0 and need128 % (2 * 1024 * 131 * 4) == 0
+    need128 = fa2.workspace_size(1, 2, 4096, 4096, 128, 1, f16)
+    assert need128 > 0 and need128 % (2 * 4096 * 131 * 4) == 0
     # float32 at D = 128 always runs whole (16-row workgroups); unsupported
     # requests ask for nothing
     assert fa2.workspace_size(1, 2, 1024, 1024, 128, 0, f32) == 0

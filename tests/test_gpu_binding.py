@@ -29,9 +29,9 @@ def test_forward_outputs():
 
 def test_forward_workspace_on_the_host_is_refused():
     import torch
-    q = torch.zeros(1, 1, 64, 64, device="cuda", dtype=torch.float16)
-    k = torch.zeros(1, 1, 8192, 64, device="cuda", dtype=torch.float16)
-    assert fa2.workspace_size(1, 1, 64, 8192, 64, False, fa2.FA2_F16) > 0
+    q = torch.zeros(1, 4, 4096, 64, device="cuda", dtype=torch.float16)
+    k = torch.zeros(1, 4, 4096, 64, device="cuda", dtype=torch.float16)
+    assert fa2.workspace_size(1, 4, 4096, 4096, 64, False, fa2.FA2_F16) > 0
     with pytest.raises(ValueError, match="workspace must be on"):
         fa2.attn_fwd(q, k, k, workspace=torch.empty(1 << 24, dtype=torch.uint8))
 
@@ -88,9 +88,9 @@ def test_side_stream_buffers_are_not_reused_early(monkeypatch):
         return t
     monkeypatch.setattr(fa2, "_alloc", spy)
 
-    q, k, v = inputs.qkv((1, 2, 1024, 64), (1, 2, 1024, 64), 21, "f16")
+    q, k, v = inputs.qkv((1, 2, 4096, 64), (1, 2, 4096, 64), 21, "f16")
     tq, tk, tv = upload(q, "f16"), upload(k, "f16"), upload(v, "f16")
-    need = fa2.workspace_size(1, 2, 1024, 1024, 64, True, fa2.FA2_F16)
+    need = fa2.workspace_size(1, 2, 4096, 4096, 64, True, fa2.FA2_F16)
     assert need > 0, "this shape is meant to split its keys"
     qd = inputs.normal((2, 4, 128), 22, 0, "f16")
     kd = inputs.normal((2, 4, 3000, 128), 22, 1, "f16")

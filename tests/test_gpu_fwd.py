@@ -248,14 +248,18 @@ def test_f32_schedules(shape, causal):
 @pytest.mark.parametrize("shape", [(1, 2, 1024, 1024, True), (1, 2, 1024, 1024, False),
                                    (1, 1, 700, 700, True), (2, 3, 300, 300, False),
                                    (1, 1, 64, 4096, False), (1, 3, 129, 2000, False),
-                                   (1, 4, 4096, 4096, True), (1, 2, 2048, 8192, False)],
+                                   (1, 2, 2048, 8192, False), (1, 1, 33, 33, True),
+                                   (2, 2, 1, 1, False), (1, 4, 4096, 4096, True),
+                                   (1, 2, 4096, 4096, False), (1, 2, 8192, 8192, False)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_mfma_split_schedules(shape, dt):
-    """f16/bf16 with few query tiles: the keys are split across workgroups
-    (workspace + combine) or not (no workspace); both against the oracle, O
-    and LSE.  The last two shapes fill more than an eighth of the compute
-    units but at most a quarter of the workgroup slots, with long keys: the
-    second split rule."""
+def test_mfma_few_tile_schedules(shape, dt):
+    """f16/bf16 with few query tiles, O and LSE against the oracle, with and
+    without a workspace.  At most one 128-row tile per eight compute units and
+    keys up to 2048: one launch of 32-row workgroups whose waves split the
+    keys (no workspace asked for).  Longer keys (with few tiles, or with the
+    tiles filling at most a quarter of the workgroup slots): the keys are split
+    across workgroups into partials that the combine kernel merges when a
+    workspace is given, and the plain kernel runs without one."""
     import torch
     B, H, Nq, Nk, causal = shape
     q, k, v = seeded(B, H, Nq, Nk, 64, dt, 13)
@@ -265,15 +269,29 @@ def test_mfma_split_schedules(shape, dt):
     tq, tk, tv = upload(q, dt), upload(k, dt), upload(v, dt)
     code = fa2.FA2_F16 if dt == "f16" else fa2.FA2_BF16
     need = fa2.workspace_size(B, H, Nq, Nk, 64, causal, code)
-    assert need > 0, "these shapes are meant to take the split path"
+    assert (need > 0) == (Nk > 2048), "the shape takes the other schedule"
     for use_ws in (True, False):
         o, lse = fa2.attn_fwd(tq, tk, tv, scale=0.125, causal=causal, return_lse=True,
                               use_workspace=use_ws)
         torch.cuda.synchronize()
         got = download_f64(o)
-        tag = "%s ws=%d" % (dt, use_ws)
-        assert_close("split schedule %s O" % tag, got, ro, edge_tol(dt, ro, got, wabs))
-        assert_close("split schedule %s LSE" % tag, download_f64(lse), rl, LSE_TOL)
+        tag = "%s ws=%d need=%d" % (dt, use_ws, need)
+        assert_close("few-tile schedule %s O" % tag, got, ro, edge_tol(dt, ro, got, wabs))
+        assert_close("few-tile schedule %s LSE" % tag, download_f64(lse), rl, LSE_TOL)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 2, 1024, 1024, True), (1, 1, 700, 700, False),
+                                   (1, 3, 129, 2000, True), (2, 1, 300, 300, True)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_mfma_few_tile_d128(shape, dt):
+    """Few query tiles at D = 128 (these keep the key split across workgroups,
+    with a workspace from the binding)."""
+    B, H, Nq, Nk, causal = shape
+    if causal and Nq != Nk:
+        Nk = Nq
+    check_full(workloads.Prefill("few tiles D128", B, H, Nq, Nk, 128, dt, 1 / np.sqrt(128), causal,
+                                 15), edge=True)
 
 
 def test_lse_optional_and_stream_order():

@@ -48,14 +48,16 @@ def _check_replays(name, refill, call):
             assert torch.equal(got, ref), "%s replay %d output %d" % (name, rep, i)
 
 
-@pytest.mark.parametrize("dt,D,causal,N", [("f16", 64, True, 1024), ("bf16", 128, False, 700),
-                                           ("f32", 64, False, 4096), ("f32", 128, True, 512)])
-def test_forward_graph(dt, D, causal, N):
+@pytest.mark.parametrize("dt,D,causal,N,H", [("f16", 64, True, 1024, 2), ("bf16", 128, False, 700, 2),
+                                             ("f32", 64, False, 4096, 1), ("f32", 128, True, 512, 2),
+                                             ("bf16", 64, True, 4096, 2)])
+def test_forward_graph(dt, D, causal, N, H):
     """attn_fwd with the LSE; the f16 causal case (16 query tiles of 128
-    rows) takes the key split, with its workspace and combine kernel."""
+    rows) runs the 32-row keys-across-waves kernel, and the bf16 N4096 case
+    the key split across workgroups with its workspace and combine kernel."""
     import torch
     from gpu_util import torch_dtype
-    B, H = (1, 1) if N == 4096 else (1, 2)
+    B = 1
     q, k, v = (torch.empty(B, H, N, D, device="cuda", dtype=torch_dtype(dt)) for _ in range(3))
     _fill((q, k, v), 1)
     ws = torch.empty(max(1, fa2.workspace_size(B, H, N, N, D, causal, fa2.dtype_code(q))),

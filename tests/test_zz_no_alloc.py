@@ -57,13 +57,13 @@ def test_two_calls_in_a_row_second_smaller(dt):
         one_pair(1, 3, 1024, 1024, 64, dt, False, 31)
         one_pair(1, 1, 300, 700, 64, dt, False, 32)
     else:
-        one_pair(1, 2, 2048, 8192, 64, dt, False, 31)
-        one_pair(1, 2, 1024, 1024, 64, dt, True, 32)
+        one_pair(1, 4, 4096, 4096, 64, dt, False, 31)
+        one_pair(1, 2, 4096, 4096, 64, dt, True, 32)
 
 
 def test_d128_split_and_no_split_shapes():
     import torch
-    one_pair(1, 1, 1024, 4096, 128, "f16", False, 33)
+    one_pair(1, 2, 4096, 4096, 128, "f16", False, 33)
     # a shape that needs no workspace runs as attn_fwd does
     q, k, v = inputs.qkv((4, 12, 512, 64), (4, 12, 512, 64), 34, "f16")
     tq, tk, tv = upload(q, "f16"), upload(k, "f16"), upload(v, "f16")
@@ -77,7 +77,7 @@ def test_d128_split_and_no_split_shapes():
 
 def test_workspace_beyond_the_array_is_refused():
     import torch
-    B, H, Nq, Nk, D = 1, 3, 1024, 4096, 128
+    B, H, Nq, Nk, D = 1, 4, 4096, 4096, 128
     need = fa2.workspace_size(B, H, Nq, Nk, D, False, fa2.FA2_F16)
     assert need > fa2.NOALLOC_SCRATCH_BYTES
     t = torch.zeros(B, H, Nq, D, device="cuda", dtype=torch.float16)
