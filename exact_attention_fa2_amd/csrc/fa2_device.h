@@ -68,17 +68,23 @@ __device__ __forceinline__ float group_reduce(float x) {
 
 __device__ __forceinline__ float xor_lane(float x, int mask) { return __shfl_xor(x, mask); }
 
+// Maximum that returns NaN when either operand is NaN (IEEE 754-2019
+// maximum).  fmaxf's NaN-dropping rule makes the compiler quiet every operand
+// it cannot prove is an arithmetic result (one extra v_max per operand for
+// MFMA accumulators and lane shuffles); this one is a single v_maximum3_f32.
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // max(x[lane], x[lane ^ 16]) and max(x[lane], x[lane ^ 32]) on the VALU
 // (v_permlane16_swap / v_permlane32_swap exchange 16-lane rows of a register
 // pair; with the same register twice, one output holds the lane's own value
 // and the other its partner's).
 __device__ __forceinline__ float max_xor16(float x) {
     const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    return fmax_nan(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float max_xor32(float x) {
     const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    return fmax_nan(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
 // f32 -> 16-bit storage, round to nearest even.

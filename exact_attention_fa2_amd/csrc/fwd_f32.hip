@@ -6,8 +6,11 @@
 // loop over keys, Online softmax, After the loop; "Flash Attention"
 // (aarnphm.xyz): Deriving the online softmax, tile form).  A workgroup owns 16
 // query rows.  Its 16 waves each walk a contiguous slice of the keys, 16 keys a
-// step, carrying the running max m, the running denominator l and the
-// unnormalised output O, rescaled by exp(m_old - m_new) whenever the max grows.
+// step, carrying a running max m, the running denominator l and the
+// unnormalised output O.  O and l are rescaled by exp(m_old - m_new) only when
+// a step's scores overtake m far enough that some exp(s - m) would pass 2^8
+// (or the row has no m yet); below that, keeping the older m changes only the
+// common factor of O and l, which the final O/l cancels.
 // At the end the 16 partial states are merged with the (m, l) monoid of "Flash
 // Attention" (section Deriving the online softmax) through LDS, then O/l and
 // LSE = m + ln l are written.
@@ -39,6 +42,11 @@ constexpr int kD = 64;
 constexpr int kQT = 16;     // query rows per workgroup
 constexpr int kWaves = 16;  // waves per workgroup (4 per SIMD), each on its own key slice
 constexpr int kStep = 16;   // keys per step
+// A step's exponentials are kept, taken against the running max as it stands,
+// when each lane's four P values sum to at most this (every P <= 2^8, far from
+// f32 overflow); otherwise the step's max is taken, O and l are rescaled and
+// the exponentials taken again.
+constexpr float kLazyCap = 256.f;
 
 // Query tile and head of this workgroup.  The grid is one-dimensional with
 // b*h varying fastest: consecutive workgroups take the same query tile of
@@ -117,14 +125,19 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
     // with d(g,i) = 16*(i/4) + 4g + i%4 -- any pairing of the contraction index
     // works, and this one lets the four lanes of a key row read 64 contiguous
     // bytes of K per load instruction.
+    // The row maxima below are taken on unscaled scores, which needs a
+    // positive scale: a negative one moves onto Q (an exact sign flip) and a
+    // zero one becomes Q = 0 with scale 1 (the scaled scores are the same).
+    const float qmul = scale_log2 < 0.f ? -1.f : scale_log2 == 0.f ? 0.f : 1.f;
+    scale_log2 = scale_log2 == 0.f ? 1.f : fabsf(scale_log2);
     float qv[D / 4];
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
         f32x4 t = __builtin_bit_cast(f32x4, load16(rq, (uint32_t)(((q0 + c) * D + 16 * j + 4 * g) * 4)));
-        qv[4 * j + 0] = t[0];
-        qv[4 * j + 1] = t[1];
-        qv[4 * j + 2] = t[2];
-        qv[4 * j + 3] = t[3];
+        qv[4 * j + 0] = t[0] * qmul;
+        qv[4 * j + 1] = t[1] * qmul;
+        qv[4 * j + 2] = t[2] * qmul;
+        qv[4 * j + 3] = t[3] * qmul;
     }
 
     const int kend = CAUSAL ? min(Nk, q0 + kQT) : Nk;
@@ -134,6 +147,7 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
     const int st1 = min(nsteps, st0 + per);
 
     float m = -INFINITY;  // running max of scaled scores, base-2 units
+    float mu = 0.f;       // m, or 0 while the row has no live key yet
     float l = 0.f;        // this lane's share of the running denominator
     f32x4 acc[4 * NH];
 #pragma unroll
@@ -162,36 +176,44 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
         }
         sacc += sacc2;
 
-        // sacc[r] = S[query q0 + c][key k0 + 4g + r]; a step past this wave's
-        // slice is masked entirely and leaves the state unchanged
+        // sacc[r] = S[query q0 + c][key k0 + 4g + r] (unscaled); a step past
+        // this wave's slice is masked entirely and leaves the state unchanged.
+        // Only steps that reach past Nk, cross the causal diagonal or lie past
+        // the slice need the per-score mask (a wave-uniform test).
         float s[4];
-        float mx = -INFINITY;
         const bool in_slice = st < st1;
+        if (in_slice && k0 + kStep <= Nk && !(CAUSAL && k0 + kStep - 1 > q0)) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = k0 + 4 * g + r;
-            bool live = in_slice && key < Nk;
-            if (CAUSAL) live = live && key <= q0 + c;
-            s[r] = live ? sacc[r] * scale_log2 : -INFINITY;
-            mx = fmaxf(mx, s[r]);
+            for (int r = 0; r < 4; ++r) s[r] = sacc[r];
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = k0 + 4 * g + r;
+                bool live = in_slice && key < Nk;
+                if (CAUSAL) live = live && key <= q0 + c;
+                s[r] = live ? sacc[r] : -INFINITY;
+            }
         }
-        mx = max_xor32(max_xor16(mx));
-        const float m_new = fmaxf(m, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        // Rescale only when some row's maximum moved: otherwise the factor
-        // is exactly 1 and the products would change nothing.
-        if (__builtin_amdgcn_ballot_w64(m_new != m) != 0) {
-            const float corr = exp2f_fast(m - m_use);
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = exp2f_fast(__builtin_fmaf(s[r], scale_log2, -mu));
+        float psum = (p[0] + p[1]) + (p[2] + p[3]);
+        // The max is only taken (and O rescaled) when a row has none yet or a
+        // score has overtaken it far enough to push some P past the cap; a
+        // rescale by exactly 1 would change nothing.
+        if (__builtin_amdgcn_ballot_w64(m == -INFINITY || psum > kLazyCap) != 0) {
+            float mx = fmax_nan(fmax_nan(s[0], s[1]), fmax_nan(s[2], s[3]));
+            mx = max_xor32(max_xor16(mx)) * scale_log2;  // base-2 units of the scaled scores
+            const float m_new = fmax_nan(m, mx);
+            mu = m_new == -INFINITY ? 0.f : m_new;
+            const float corr = exp2f_fast(m - mu);
             l *= corr;
 #pragma unroll
             for (int j = 0; j < 4 * NH; ++j) acc[j] *= corr;
-        }
-        float p[4];
-        float psum = 0.f;
+            m = m_new;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            p[r] = exp2f_fast(s[r] - m_use);
-            psum += p[r];
+            for (int r = 0; r < 4; ++r) p[r] = exp2f_fast(__builtin_fmaf(s[r], scale_log2, -mu));
+            psum = (p[0] + p[1]) + (p[2] + p[3]);
         }
         l += psum;
         // O^T += V^T P^T: slot g pairs key k0 + 4g + t; row m of tile 4h + j is
@@ -204,7 +226,6 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
                 for (int j = 0; j < 4; ++j)
                     acc[4 * h + j] =
                         __builtin_amdgcn_mfma_f32_16x16x4f32(cur.v[t][h][j], p[t], acc[4 * h + j], 0, 0, 0);
-        m = m_new;
     };
 
     // Steps run in pairs, unconditionally, so each step's prefetch has a
@@ -321,15 +342,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void kernel(
     const auto rk = make_rsrc(Kh, (uint32_t)Nk * kD * 4);
     const auto rv = make_rsrc(Vh, (uint32_t)Nk * kD * 4);
 
-    // Q^T operand, pairing d = 16*(i/4) + 4g + i%4 as in the kernel above.
+    // Q^T operand, pairing d = 16*(i/4) + 4g + i%4 as in the kernel above,
+    // with the sign of the scale moved onto Q as there.
+    const float qmul = scale_log2 < 0.f ? -1.f : scale_log2 == 0.f ? 0.f : 1.f;
+    scale_log2 = scale_log2 == 0.f ? 1.f : fabsf(scale_log2);
     float qv[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         f32x4 t = __builtin_bit_cast(f32x4, load16(rq, (uint32_t)(((qt0 + c) * kD + 16 * j + 4 * g) * 4)));
-        qv[4 * j + 0] = t[0];
-        qv[4 * j + 1] = t[1];
-        qv[4 * j + 2] = t[2];
-        qv[4 * j + 3] = t[3];
+        qv[4 * j + 0] = t[0] * qmul;
+        qv[4 * j + 1] = t[1] * qmul;
+        qv[4 * j + 2] = t[2] * qmul;
+        qv[4 * j + 3] = t[3] * qmul;
     }
 
     // Steps of 16 keys: the chunk's steps, then this sub-slice's share.
@@ -366,7 +390,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void kernel(
         }
     };
 
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, mu = 0.f, l = 0.f;  // mu: m, or 0 while m is -inf
     f32x4 acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -395,37 +419,47 @@ __global__ __launch_bounds__(kWaves * 64, 1) void kernel(
                                                         0, 0, 0);
         }
         sacc += sacc2;
+        // unscaled scores, masked only on steps that need it; then the
+        // exponentials against the running max, kept unless the max must move
+        // (the rule of the kernel above)
         const bool in_slice = st < st1;
         float sv[4];
-        float mx = -INFINITY;
+        if (in_slice && k0 + kStep <= Nk && !(CAUSAL && k0 + kStep - 1 > qt0)) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = k0 + 4 * g + r;
-            bool live = in_slice && key < Nk;
-            if (CAUSAL) live = live && key <= qt0 + c;
-            sv[r] = live ? sacc[r] * scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sv[r]);
+            for (int r = 0; r < 4; ++r) sv[r] = sacc[r];
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = k0 + 4 * g + r;
+                bool live = in_slice && key < Nk;
+                if (CAUSAL) live = live && key <= qt0 + c;
+                sv[r] = live ? sacc[r] : -INFINITY;
+            }
         }
-        mx = max_xor32(max_xor16(mx));
-        const float m_new = fmaxf(m, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float corr = exp2f_fast(m - m_use);
         float p[4];
-        float psum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            p[r] = exp2f_fast(sv[r] - m_use);
-            psum += p[r];
+        for (int r = 0; r < 4; ++r) p[r] = exp2f_fast(__builtin_fmaf(sv[r], scale_log2, -mu));
+        float psum = (p[0] + p[1]) + (p[2] + p[3]);
+        if (__builtin_amdgcn_ballot_w64(m == -INFINITY || psum > kLazyCap) != 0) {
+            float mx = fmax_nan(fmax_nan(sv[0], sv[1]), fmax_nan(sv[2], sv[3]));
+            mx = max_xor32(max_xor16(mx)) * scale_log2;
+            const float m_new = fmax_nan(m, mx);
+            mu = m_new == -INFINITY ? 0.f : m_new;
+            const float corr = exp2f_fast(m - mu);
+            l *= corr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] *= corr;
+            m = m_new;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = exp2f_fast(__builtin_fmaf(sv[r], scale_log2, -mu));
+            psum = (p[0] + p[1]) + (p[2] + p[3]);
         }
-        l = l * corr + psum;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] *= corr;
+        l += psum;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[t][j], p[t], acc[j], 0, 0, 0);
-        m = m_new;
     };
 
     // Iterations: every sub-slice advances one step per iteration.  On entry

@@ -204,6 +204,62 @@ def test_large_score_shift_is_safe(dt):
     assert_close("shift LSE " + dt, lse, rl, LSE_TOL)
 
 
+@pytest.mark.parametrize("order", ["rising", "falling"])
+@pytest.mark.parametrize("dt,shape", [("f32", (1, 1, 1024, 1024)), ("f32", (4, 16, 256, 256)),
+                                      ("f16", (1, 2, 1024, 1024)), ("bf16", (2, 4, 1024, 1024))],
+                         ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_running_max_moves_often(order, dt, shape):
+    """Scores that grow (or shrink) steadily along the keys: with Q[..., 0] = 4
+    and K[j, 0] += 0.05 j, scale 0.5 adds 0.1 j to every score of key j (up to
+    about 100), so while a wave walks its keys the running max passes its
+    previous value by far more than the kernels' rescale threshold again and
+    again ("rising"), or is set by the first keys and never moves
+    ("falling").  Every schedule runs (f32: with and without a workspace, and
+    the shared-K/V kernel at 4x16 heads of 256 rows)."""
+    import torch
+    B, H, Nq, Nk = shape
+    q, k, v = seeded(B, H, Nq, Nk, 64, dt, 14)
+    q64, k64 = inputs.to_f64(q, dt), inputs.to_f64(k, dt)
+    ramp = 0.05 * np.arange(Nk)
+    q64[..., 0] = 4.0
+    k64[..., 0] += ramp if order == "rising" else ramp[::-1]
+    def store(x):
+        x32 = x.astype(np.float32)
+        return inputs.f32_to_bf16_bits(x32) if dt == "bf16" else x32.astype(inputs.storage_numpy_dtype(dt))
+    q, k = store(q64), store(k64)
+    q64, k64, v64 = (inputs.to_f64(x, dt) for x in (q, k, v))
+    tq, tk, tv = upload(q, dt), upload(k, dt), upload(v, dt)
+    for causal in (False, True):
+        ro, rl = oracle.attn(q64, k64, v64, 0.5, causal)
+        wabs = oracle.attn(q64, k64, np.abs(v64), 0.5, causal)[0]
+        for use_ws in ((True, False) if dt == "f32" else (True,)):
+            o, lse = fa2.attn_fwd(tq, tk, tv, scale=0.5, causal=causal, return_lse=True,
+                                  use_workspace=use_ws)
+            torch.cuda.synchronize()
+            o = download_f64(o)
+            tag = "%s %s causal=%d ws=%d" % (order, dt, causal, use_ws)
+            assert_close(tag + " O", o, ro, TOL["f32"] if dt == "f32" else edge_tol(dt, ro, o, wabs))
+            assert_close(tag + " LSE", download_f64(lse), rl, LSE_TOL)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 2.0])
+def test_f32_shared_kernel_unusual_scales(scale):
+    """The float32 shared-K/V kernel (256 groups of 64 rows: one per compute
+    unit) with scale 0, a negative scale and a large one, causal and not."""
+    import torch
+    q, k, v = seeded(4, 16, 256, 256, 64, "f32", 15)
+    q64, k64, v64 = (inputs.to_f64(x, "f32") for x in (q, k, v))
+    tq, tk, tv = upload(q, "f32"), upload(k, "f32"), upload(v, "f32")
+    for causal in (False, True):
+        o, lse = fa2.attn_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=True)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attn(q64, k64, v64, scale, causal)
+        assert_close("f32 shared scale %g causal=%d O" % (scale, causal), download_f64(o), ro,
+                     TOL["f32"])
+        assert_close("f32 shared scale %g causal=%d LSE" % (scale, causal), download_f64(lse), rl,
+                     LSE_TOL)
+
+
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 def test_deterministic(dt):
     import torch
