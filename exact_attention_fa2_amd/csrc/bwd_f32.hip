@@ -192,13 +192,21 @@ __global__ __launch_bounds__(kW * 64, 1) void bwd_f32_dq_kernel(
         const f32x4 dp = product(cur.v, gv);  // dP, same slots
         const bool in_slice = st < st1;
         float ds[4];
+        // the per-score mask only on steps that reach past Nk or Nq, cross the
+        // diagonal or lie past this wave's slice (a wave-uniform test)
+        if (in_slice && k0 + kStep <= Nk && q0 + kT <= Nq && !(CAUSAL && k0 + kStep - 1 > q0)) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = k0 + 4 * g + r;
-            bool live = in_slice && qlive && key < Nk;
-            if (CAUSAL) live = live && key <= myq;
-            const float p = live ? exp2f_fast(__builtin_fmaf(s[r], scale_log2, -l2)) : 0.f;
-            ds[r] = p * (dp[r] - dl);
+            for (int r = 0; r < 4; ++r)
+                ds[r] = exp2f_fast(__builtin_fmaf(s[r], scale_log2, -l2)) * (dp[r] - dl);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = k0 + 4 * g + r;
+                bool live = in_slice && qlive && key < Nk;
+                if (CAUSAL) live = live && key <= myq;
+                const float p = live ? exp2f_fast(__builtin_fmaf(s[r], scale_log2, -l2)) : 0.f;
+                ds[r] = p * (dp[r] - dl);
+            }
         }
 #pragma unroll
         for (int h = 0; h < NH; ++h) accumulate(acc + 4 * h, cur.kc[h], ds);
@@ -333,13 +341,23 @@ __global__ __launch_bounds__(kW * 64, 1) void bwd_f32_dkdv_kernel(
         }
         const bool in_slice = st < st1;
         float p[4], ds[4];
+        // the per-score mask only on steps that reach past Nq or Nk, cross the
+        // diagonal or lie past this wave's slice (a wave-uniform test)
+        if (in_slice && q0 + kStep <= Nq && k0 + kT <= Nk && !(CAUSAL && k0 + kT - 1 > q0)) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int q = q0 + 4 * g + r;
-            bool live = in_slice && klive && q < Nq;
-            if (CAUSAL) live = live && myk <= q;
-            p[r] = live ? exp2f_fast(__builtin_fmaf(s[r], scale_log2, -cur.l[r] * kLog2e)) : 0.f;
-            ds[r] = p[r] * (dp[r] - cur.d[r]);
+            for (int r = 0; r < 4; ++r) {
+                p[r] = exp2f_fast(__builtin_fmaf(s[r], scale_log2, -cur.l[r] * kLog2e));
+                ds[r] = p[r] * (dp[r] - cur.d[r]);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int q = q0 + 4 * g + r;
+                bool live = in_slice && klive && q < Nq;
+                if (CAUSAL) live = live && myk <= q;
+                p[r] = live ? exp2f_fast(__builtin_fmaf(s[r], scale_log2, -cur.l[r] * kLog2e)) : 0.f;
+                ds[r] = p[r] * (dp[r] - cur.d[r]);
+            }
         }
         accumulate(dv, cur.gc, p);
         accumulate(dk, cur.qc, ds);
