@@ -82,18 +82,25 @@ struct KVRegs {
     f32x4 v[4][D / 64];  // v[t][h] = V[key k0 + 4g + t][64h + 4c .. 64h + 4c + 3], t = 0..3
 };
 
+// The 16 keys from k0 on.  The buffer descriptors start at key k0 and cover
+// the keys left (none past Nk), so the per-lane offsets stay the same from
+// step to step and the step's position is scalar arithmetic on the
+// descriptor; keys at or past Nk read as zeros.
 template <int D>
-__device__ __forceinline__ void load_kv(KVRegs<D> &r, __amdgpu_buffer_rsrc_t rk,
-                                        __amdgpu_buffer_rsrc_t rv, int k0, int g, int c) {
+__device__ __forceinline__ void load_kv(KVRegs<D> &r, const float *Kh, const float *Vh, int Nk,
+                                        int k0, int g, int c) {
+    const uint32_t bytes = k0 < Nk ? (uint32_t)(Nk - k0) * D * 4 : 0u;
+    const auto rk = make_rsrc(Kh + (size_t)k0 * D, bytes);
+    const auto rv = make_rsrc(Vh + (size_t)k0 * D, bytes);
 #pragma unroll
     for (int j = 0; j < D / 16; ++j)
-        r.k[j] = __builtin_bit_cast(f32x4, load16(rk, (uint32_t)(((k0 + c) * D + 16 * j + 4 * g) * 4)));
+        r.k[j] = __builtin_bit_cast(f32x4, load16(rk, (uint32_t)((c * D + 16 * j + 4 * g) * 4)));
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int h = 0; h < D / 64; ++h)
             r.v[t][h] = __builtin_bit_cast(
-                f32x4, load16(rv, (uint32_t)(((k0 + 4 * g + t) * D + 64 * h + 4 * c) * 4)));
+                f32x4, load16(rv, (uint32_t)(((4 * g + t) * D + 64 * h + 4 * c) * 4)));
 }
 
 template <int D, bool CAUSAL>
@@ -118,8 +125,6 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
     const float *Kh = K + (size_t)bh * Nk * D;
     const float *Vh = V + (size_t)bh * Nk * D;
     const auto rq = make_rsrc(Qh, (uint32_t)Nq * D * 4);
-    const auto rk = make_rsrc(Kh, (uint32_t)Nk * D * 4);
-    const auto rv = make_rsrc(Vh, (uint32_t)Nk * D * 4);
 
     // Q^T operand of S^T = K Q^T: slot i of lane (g,c) is Q[q0 + c][d(g,i)]
     // with d(g,i) = 16*(i/4) + 4g + i%4 -- any pairing of the contraction index
@@ -161,7 +166,7 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
     // wait for `cur` never also waits for `nxt`.
     auto step = [&](int st, const KVRegs<D> &cur, KVRegs<D> &nxt) {
         const int k0 = st * kStep;
-        load_kv<D>(nxt, rk, rv, k0 + kStep, g, c);
+        load_kv<D>(nxt, Kh, Vh, Nk, k0 + kStep, g, c);
         // keep the loads here: without this the scheduler sinks them next to
         // their use in the following step, which serialises load and compute
         __builtin_amdgcn_sched_barrier(0);
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
     // Steps run in pairs, unconditionally, so each step's prefetch has a
     // use on every path and the compiler keeps it where it is issued.
     KVRegs<D> ra, rb;
-    load_kv<D>(ra, rk, rv, st0 * kStep, g, c);
+    load_kv<D>(ra, Kh, Vh, Nk, st0 * kStep, g, c);
     for (int st = st0; st < st1; st += 2) {
         step(st, ra, rb);
         step(st + 1, rb, ra);
