@@ -306,6 +306,22 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
                                                      off, 0, 0, 0);
         }
     };
+    // The same for k0 >= 0 through a descriptor that starts at key k0 and
+    // covers the keys left (none past Nk): the per-lane offsets do not
+    // change from block to block, and the block's position is scalar work.
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // for the LDS destinations
+    auto dma_at = [&](const uint16_t *X, uint16_t *dst, int k0, bool r_is_k) {
+        const auto r = make_rsrc(X + (size_t)k0 * kD, k0 < Nk ? (uint32_t)(Nk - k0) * kD * 2 : 0u);
+#pragma unroll
+        for (int i = 0; i < UPL; ++i) {
+            const int unit = (UPL * wave + i) * 64 + lane;
+            const int row = unit / CPR;
+            const int ch = (unit % CPR) ^ (r_is_k ? kswz<D>(row) : vswz<D>(row));
+            const uint32_t off = (uint32_t)((row * kD + ch * 8) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (UPL * wave_s + i) * 512), 16,
+                                                     off, 0, 0, 0);
+        }
+    };
 
     // LDS offsets that do not change from tile to tile (relative to the
     // tile's first row; both halves of a 64-row buffer share the swizzle).
@@ -481,8 +497,8 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
     auto block = [&](int b, const uint16_t *kc, uint16_t *kd, const uint16_t *vc, uint16_t *vd,
                      f32x16 *sa, f32x16 *sb) {
         if (b + 1 < b1) {
-            dma(rv, vd, (b + 1) * kBC, false);
-            dma(rk, kd, (b + 1) * kBC + 32, true);
+            dma_at(Vh, vd, (b + 1) * kBC, false);
+            dma_at(Kh, kd, (b + 1) * kBC + 32, true);
         }
         run_tile(2 * b, kc, vc, sa, sb);
         run_tile(2 * b + 1, kc + 32 * kD, vc + 32 * kD, sb, sa);
