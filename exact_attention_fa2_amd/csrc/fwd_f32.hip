@@ -89,9 +89,10 @@ struct KVRegs {
 template <int D>
 __device__ __forceinline__ void load_kv(KVRegs<D> &r, const float *Kh, const float *Vh, int Nk,
                                         int k0, int g, int c) {
-    const uint32_t bytes = k0 < Nk ? (uint32_t)(Nk - k0) * D * 4 : 0u;
-    const auto rk = make_rsrc(Kh + (size_t)k0 * D, bytes);
-    const auto rv = make_rsrc(Vh + (size_t)k0 * D, bytes);
+    const int kb = k0 < Nk ? k0 : Nk;  // base within the tensor; no records past Nk
+    const uint32_t bytes = (uint32_t)(Nk - kb) * D * 4;
+    const auto rk = make_rsrc(Kh + (size_t)kb * D, bytes);
+    const auto rv = make_rsrc(Vh + (size_t)kb * D, bytes);
 #pragma unroll
     for (int j = 0; j < D / 16; ++j)
         r.k[j] = __builtin_bit_cast(f32x4, load16(rk, (uint32_t)((c * D + 16 * j + 4 * g) * 4)));

@@ -311,7 +311,8 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
     // change from block to block, and the block's position is scalar work.
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // for the LDS destinations
     auto dma_at = [&](const uint16_t *X, uint16_t *dst, int k0, bool r_is_k) {
-        const auto r = make_rsrc(X + (size_t)k0 * kD, k0 < Nk ? (uint32_t)(Nk - k0) * kD * 2 : 0u);
+        const int kb = k0 < Nk ? k0 : Nk;  // base within the tensor; no records past Nk
+        const auto r = make_rsrc(X + (size_t)kb * kD, (uint32_t)(Nk - kb) * kD * 2);
 #pragma unroll
         for (int i = 0; i < UPL; ++i) {
             const int unit = (UPL * wave + i) * 64 + lane;
