@@ -136,21 +136,36 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
     // zero one becomes Q = 0 with scale 1 (the scaled scores are the same).
     const float qmul = scale_log2 < 0.f ? -1.f : scale_log2 == 0.f ? 0.f : 1.f;
     scale_log2 = scale_log2 == 0.f ? 1.f : fabsf(scale_log2);
-    float qv[D / 4];
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-        f32x4 t = __builtin_bit_cast(f32x4, load16(rq, (uint32_t)(((q0 + c) * D + 16 * j + 4 * g) * 4)));
-        qv[4 * j + 0] = t[0] * qmul;
-        qv[4 * j + 1] = t[1] * qmul;
-        qv[4 * j + 2] = t[2] * qmul;
-        qv[4 * j + 3] = t[3] * qmul;
-    }
 
     const int kend = CAUSAL ? min(Nk, q0 + kQT) : Nk;
     const int nsteps = (kend + kStep - 1) / kStep;
     const int per = (nsteps + W - 1) / W;
     const int st0 = wave * per;
     const int st1 = min(nsteps, st0 + per);
+
+    // This wave's first K/V operands go out before Q, the larger load first.
+    KVRegs<D> ra, rb;
+    load_kv<D>(ra, Kh, Vh, Nk, st0 * kStep, g, c);
+
+    // The workgroup's Q tile (16 rows) is read from memory once, through the
+    // merge area of LDS (free until the end), instead of once per wave.
+    {
+        float *sq = &s_o[0][0][0];
+        for (int e = threadIdx.x; e < kQT * D / 4; e += W * 64)
+            *reinterpret_cast<f32x4 *>(sq + 4 * e) = __builtin_bit_cast(f32x4, load16(rq, (uint32_t)((q0 * D + 4 * e) * 4)));
+        __syncthreads();
+    }
+    float qv[D / 4];
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(&s_o[0][0][0] + c * D + 16 * j + 4 * g);
+        qv[4 * j + 0] = t[0] * qmul;
+        qv[4 * j + 1] = t[1] * qmul;
+        qv[4 * j + 2] = t[2] * qmul;
+        qv[4 * j + 3] = t[3] * qmul;
+    }
+    // every wave has its Q before the merge area is written again
+    __syncthreads();
 
     float m = -INFINITY;  // running max of scaled scores, base-2 units
     float mu = 0.f;       // m, or 0 while the row has no live key yet
@@ -236,8 +251,6 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
 
     // Steps run in pairs, unconditionally, so each step's prefetch has a
     // use on every path and the compiler keeps it where it is issued.
-    KVRegs<D> ra, rb;
-    load_kv<D>(ra, Kh, Vh, Nk, st0 * kStep, g, c);
     for (int st = st0; st < st1; st += 2) {
         step(st, ra, rb);
         step(st + 1, rb, ra);
@@ -260,40 +273,35 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
     __syncthreads();
 
     // Merge the wave states of each row ((m, l) merge of the online softmax).
-    // First one thread per row: the row's max m and denominator l, its LSE,
-    // the weight 2^(m_w - m) of every wave's unnormalised O, and 1 / l.  The
-    // row's s_m entries, read only by this thread, then hold the weights and
-    // s_l[0][row] holds 1 / l, so no more LDS is needed.
-    if (threadIdx.x < kQT) {
-        const int row = threadIdx.x;
-        float mg = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < W; ++w) mg = fmaxf(mg, s_m[w][row]);
-        float wt[W];
-        float lg = 0.f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-            const float mw = s_m[w][row];
-            wt[w] = mw == -INFINITY ? 0.f : exp2f_fast(mw - mg);
-            lg += wt[w] * s_l[w][row];
+    // First W lanes per row, one per wave state: the row's max m by a
+    // reduction over those lanes, each state's weight 2^(m_w - m), and l as
+    // the weighted sum of the states' l.  The weights replace the row's s_m
+    // entries and s_l[0][row] holds 1 / l (each row's lanes sit in one wave and
+    // read their entries before any of them is written).
+    if (threadIdx.x < kQT * W) {
+        const int row = threadIdx.x / W, w = threadIdx.x % W;
+        const float mw = s_m[w][row];
+        const float mg = group_reduce<W, true>(mw);
+        const float wt = mw == -INFINITY ? 0.f : exp2f_fast(mw - mg);
+        const float lg = group_reduce<W>(wt * s_l[w][row]);
+        s_m[w][row] = wt;
+        if (w == 0) {
+            s_l[0][row] = 1.f / lg;
+            const int qrow = q0 + row;
+            if (LSE && qrow < Nq) LSE[(size_t)bh * Nq + qrow] = (mg + log2f_fast(lg)) * kLn2;
         }
-#pragma unroll
-        for (int w = 0; w < W; ++w) s_m[w][row] = wt[w];
-        s_l[0][row] = 1.f / lg;
-        const int qrow = q0 + row;
-        if (LSE && qrow < Nq) LSE[(size_t)bh * Nq + qrow] = (mg + log2f_fast(lg)) * kLn2;
     }
     __syncthreads();
-    // Then one output element per thread and pass (one pass at D = 64, four
-    // at D = 128): the weighted sum of the waves' O, divided by l once.
-    for (int e = threadIdx.x; e < kQT * D; e += W * 64) {
-        const int row = e / D;
-        const int d = e % D;
-        float o0 = 0.f;
+    // Then four consecutive output columns per thread: the weighted sum of
+    // the states' O, divided by l once.
+    for (int e = threadIdx.x; e < kQT * D / 4; e += W * 64) {
+        const int row = e / (D / 4);
+        const int d = 4 * (e % (D / 4));
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < W; ++w) o0 = __builtin_fmaf(s_m[w][row], s_o[w][row][d], o0);
+        for (int w = 0; w < W; ++w) o += s_m[w][row] * *reinterpret_cast<const f32x4 *>(&s_o[w][row][d]);
         const int qrow = q0 + row;
-        if (qrow < Nq) O[((size_t)bh * Nq + qrow) * D + d] = o0 * s_l[0][row];
+        if (qrow < Nq) *reinterpret_cast<f32x4 *>(O + ((size_t)bh * Nq + qrow) * D + d) = o * s_l[0][row];
     }
 }
 
