@@ -1,17 +1,18 @@
-// fwd_f32.hip -- exact attention forward, float32 in and out, D = 64, on the
-// float32 matrix cores of gfx950 (v_mfma_f32_16x16x4_f32: full f32 operands,
-// f32 accumulation; nothing is rounded to a narrower type).
+// fwd_f32.hip -- exact attention forward, float32 in and out, D = 64 or 128,
+// on the float32 matrix cores of gfx950 (v_mfma_f32_16x16x4_f32: full f32
+// operands, f32 accumulation; nothing is rounded to a narrower type).
 //
 // Method ("Flash attention, f32": sections One block of queries per CTA, The
 // loop over keys, Online softmax, After the loop; "Flash Attention"
 // (aarnphm.xyz): Deriving the online softmax, tile form).  A workgroup owns 16
-// query rows.  Its 16 waves each walk a contiguous slice of the keys, 16 keys a
-// step, carrying a running max m, the running denominator l and the
-// unnormalised output O.  O and l are rescaled by exp(m_old - m_new) only when
-// a step's scores overtake m far enough that some exp(s - m) would pass 2^8
-// (or the row has no m yet); below that, keeping the older m changes only the
-// common factor of O and l, which the final O/l cancels.
-// At the end the 16 partial states are merged with the (m, l) monoid of "Flash
+// query rows, read from memory once into LDS and from there into every wave's
+// registers.  Its 16 waves (8 at D = 128) each walk a contiguous slice of the
+// keys, 16 keys a step, carrying a running max m, the running denominator l
+// and the unnormalised output O.  O and l are rescaled by exp(m_old - m_new)
+// only when a step's scores overtake m far enough that some exp(s - m) would
+// pass 2^8 (or the row has no m yet); below that, keeping the older m changes
+// only the common factor of O and l, which the final O/l cancels.  At the end
+// the waves' partial states are merged with the (m, l) monoid of "Flash
 // Attention" (section Deriving the online softmax) through LDS, then O/l and
 // LSE = m + ln l are written.
 //
