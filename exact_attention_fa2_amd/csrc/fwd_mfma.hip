@@ -926,6 +926,10 @@ struct Plan {
 #define FA2_MFMA_SPLIT_LONG 32  // also split when the tiles fill at most a quarter of the slots
                                 // and the keys span at least this many 64-key blocks (0: never)
 #endif
+#ifndef FA2_MFMA_SPLIT_LONG_HALF
+#define FA2_MFMA_SPLIT_LONG_HALF 128  // ... or at most half of the slots and at least this many
+                                      // blocks (0: never)
+#endif
 
 // Query groups per wave: 64-row waves when the 256-row tiles make whole
 // rounds of two per compute unit.  Keys: split the keys of each query tile
@@ -956,10 +960,13 @@ Plan plan(int B, int H, int Nq, int Nk, int D, int num_cus) {
     } else if (FA2_MFMA_SPLIT_LONG > 0 && nt > 0 && nblk >= FA2_MFMA_SPLIT_LONG) {
         // Long keys with the tiles filling at most a quarter of the resident
         // workgroup slots: cut the keys so the chunks fill the slots (the
-        // partials then cost little next to the work of each chunk; at half
-        // the slots writing them costs more than the idle slots).
+        // partials then cost little next to the work of each chunk).  At half
+        // the slots only with very long keys: B4 H12 with 1024 queries split
+        // in two measured 38.6 -> 47.3 us at 2048 keys, no change at 4096,
+        // 140.1 -> 127.3 us at 8192.
         const long long slots = (long long)num_cus * (p.qg == 1 && D == 64 ? 3 : 2);
-        if (4 * nt <= slots) {
+        if (4 * nt <= slots ||
+            (FA2_MFMA_SPLIT_LONG_HALF > 0 && nblk >= FA2_MFMA_SPLIT_LONG_HALF && 2 * nt <= slots)) {
             const long long c = std::min<long long>(slots / nt, nblk / 16);
             p.chunks = (int)std::max<long long>(1, std::min<long long>(c, 32));
         }

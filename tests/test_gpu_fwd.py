@@ -337,6 +337,33 @@ def test_mfma_few_tile_schedules(shape, dt):
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_long_keys_split_at_half_the_slots(dt):
+    """200 query tiles of 128 rows (more than a quarter, at most half of the
+    768 workgroup slots of 256 compute units) over 8192 keys: the keys are
+    split across workgroups when a workspace is given (not with 4096 keys).
+    Three heads (first, middle, last) against the oracle, with and without a
+    workspace."""
+    import torch
+    B, H, Nq, Nk = 1, 25, 1024, 8192
+    code = fa2.FA2_F16 if dt == "f16" else fa2.FA2_BF16
+    need = fa2.workspace_size(B, H, Nq, Nk, 64, False, code)
+    assert need > 0 and fa2.workspace_size(B, H, Nq, 4096, 64, False, code) == 0
+    q, k, v = seeded(B, H, Nq, Nk, 64, dt, 16)
+    tq, tk, tv = upload(q, dt), upload(k, dt), upload(v, dt)
+    heads = [0, 12, 24]
+    q64, k64, v64 = (inputs.to_f64(x, dt)[:, heads] for x in (q, k, v))
+    ro, rl = oracle.attn(q64, k64, v64, 0.125, False)
+    wabs = oracle.attn(q64, k64, np.abs(v64), 0.125, False)[0]
+    for use_ws in (True, False):
+        o, lse = fa2.attn_fwd(tq, tk, tv, scale=0.125, return_lse=True, use_workspace=use_ws)
+        torch.cuda.synchronize()
+        got = download_f64(o)[:, heads]
+        tag = "%s ws=%d" % (dt, use_ws)
+        assert_close("half-slot split %s O" % tag, got, ro, edge_tol(dt, ro, got, wabs))
+        assert_close("half-slot split %s LSE" % tag, download_f64(lse)[:, heads], rl, LSE_TOL)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", [(1, 2, 1024, 1024, True), (1, 1, 700, 700, False),
                                    (1, 3, 129, 2000, True), (2, 1, 300, 300, True)],
                          ids=lambda s: "x".join(map(str, s)))
