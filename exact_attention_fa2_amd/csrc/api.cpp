@@ -203,8 +203,7 @@ FA2_API fa2_status attn_decode_combine(const float *o_part, const float *m_part,
     if (D != 64 && D != 128) return FA2_ERR_UNSUPPORTED;
     if ((long long)B * H == 0) return FA2_OK;
     if (!o_part || !m_part || !l_part || !o) return FA2_ERR_NULL;
-    if (((uintptr_t)o_part & 3u) || ((uintptr_t)m_part & 3u) || ((uintptr_t)l_part & 3u) ||
-        !aligned16(o))
+    if (!aligned16(o_part) || ((uintptr_t)m_part & 3u) || ((uintptr_t)l_part & 3u) || !aligned16(o))
         return FA2_ERR_ALIGN;
     if ((long long)B * H > 0x7FFFFFFF) return FA2_ERR_UNSUPPORTED;
     if (!current_device()) return FA2_ERR_DEVICE;

@@ -13,10 +13,11 @@
 // workgroup merges its 4 waves x R row groups with the (m, l) monoid in LDS
 // before writing one unnormalised partial (O_s, m_s, l_s).
 //
-// Combine kernel: one workgroup per (b,h), one thread per output column;
-// weights exp(m_s - m_g), a single division by l_g at the end.  It also
-// merges the key-split partials of the forward kernels (one workgroup per
-// query row); those may carry a second denominator for the LSE.
+// Combine kernel: one output row per (b,h), four output columns per thread
+// and several rows per workgroup; weights exp(m_s - m_g), a single division
+// by l_g at the end.  It also merges the key-split partials of the forward
+// kernels (one output row per query row); those may carry a second
+// denominator for the LSE.
 #include "fa2_device.h"
 #include "fa2_internal.h"
 
@@ -173,36 +174,64 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(
     }
 }
 
-template <int DT, int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float *__restrict__ o_part,
-                                                           const float *__restrict__ m_part,
-                                                           const float *__restrict__ l_part,
-                                                           const float *__restrict__ l2_part,
-                                                           void *__restrict__ O,
-                                                           float *__restrict__ LSE, int n_splits) {
-    const size_t bh = blockIdx.x;  // one output row (a (b,h) pair for decode)
-    const int d = threadIdx.x;
+// CPT output columns per thread (1 or 4), D/CPT threads per row, and
+// blockDim.x / (D/CPT) rows per workgroup.  Many rows (the forward's
+// key-split partials of tens of thousands of rows) take four columns per
+// thread and up to 256 threads per workgroup: one single-wave workgroup per
+// row left those bound by workgroup dispatch.  Few rows (decode, few-tile
+// splits) take one row per workgroup and one column per thread, which keeps
+// more loads in flight per row.
+template <int CPT>
+struct Cols;
+template <>
+struct Cols<1> {
+    typedef float type;
+};
+template <>
+struct Cols<4> {
+    typedef f32x4 type;
+};
+
+template <int DT, int D, int CPT>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float *__restrict__ o_part,
+                                                             const float *__restrict__ m_part,
+                                                             const float *__restrict__ l_part,
+                                                             const float *__restrict__ l2_part,
+                                                             void *__restrict__ O,
+                                                             float *__restrict__ LSE, size_t rows,
+                                                             int n_splits) {
+    typedef typename Cols<CPT>::type vec;
+    constexpr int TPR = D / CPT;
+    // output row ((b,h) for decode); with one row per workgroup it is
+    // wave-uniform, and the row's m and l come through scalar loads
+    const size_t bh = CPT == 1 ? (size_t)blockIdx.x
+                               : (size_t)blockIdx.x * (blockDim.x / TPR) + threadIdx.x / TPR;
+    const int d = CPT * (threadIdx.x % TPR);
+    if (bh >= rows) return;
     const float *mp = m_part + bh * n_splits;
     const float *lp = l_part + bh * n_splits;
-    const float *op = o_part + bh * n_splits * D;
+    const float *op = o_part + bh * n_splits * D + d;
     float mg = -INFINITY;
 #pragma unroll 8
     for (int s = 0; s < n_splits; ++s) mg = fmaxf(mg, mp[s]);
-    float lg = 0.f, lg2 = 0.f, acc = 0.f;
+    float lg = 0.f, lg2 = 0.f;
+    vec acc = {};
 #pragma unroll 8
     for (int s = 0; s < n_splits; ++s) {
         const float ms = mp[s];
         const float wt = ms == -INFINITY ? 0.f : exp2f_fast((ms - mg) * kLog2e);
         lg += wt * lp[s];
         if (l2_part) lg2 += wt * l2_part[bh * n_splits + s];
-        acc += wt * op[(size_t)s * D + d];
+        acc += wt * *reinterpret_cast<const vec *>(op + (size_t)s * D);
     }
-    const float o = acc / lg;
+    const vec o = acc / lg;
     if constexpr (DT == 0) {
-        ((float *)O)[bh * D + d] = o;
+        *reinterpret_cast<vec *>((float *)O + bh * D + d) = o;
+    } else if constexpr (CPT == 1) {
+        ((uint16_t *)O)[bh * D + d] = (uint16_t)(pack2<DT>(o, 0.f) & 0xFFFF);
     } else {
-        const uint32_t w = pack2<DT>(o, 0.f);
-        ((uint16_t *)O)[bh * D + d] = (uint16_t)(w & 0xFFFF);
+        const u32x2 w = {pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3])};
+        *reinterpret_cast<u32x2 *>((uint16_t *)O + bh * D + d) = w;
     }
     if (LSE && d == 0) LSE[bh] = mg + log2f_fast(l2_part ? lg2 : lg) * kLn2;
 }
@@ -219,11 +248,19 @@ template <int DT>
 fa2_status combine_dt(const float *op, const float *mp, const float *lp, const float *lp2, void *o,
                       float *lse, size_t rows, int D, int ns, hipStream_t st) {
     if (rows > 0x7FFFFFFF) return FA2_ERR_UNSUPPORTED;
+    if (rows * D < (size_t)1 << 20) {  // one row per workgroup, one column per thread
+        if (D == 64)
+            return launch(decode_combine_kernel<DT, 64, 1>, dim3((unsigned)rows), dim3(64), st, op, mp,
+                          lp, lp2, o, lse, rows, ns);
+        return launch(decode_combine_kernel<DT, 128, 1>, dim3((unsigned)rows), dim3(128), st, op, mp, lp,
+                      lp2, o, lse, rows, ns);
+    }
+    // four columns per thread, 256 threads: 16 (D = 64) or 8 (D = 128) rows
     if (D == 64)
-        return launch(decode_combine_kernel<DT, 64>, dim3((unsigned)rows), dim3(64), st, op, mp, lp,
-                      lp2, o, lse, ns);
-    return launch(decode_combine_kernel<DT, 128>, dim3((unsigned)rows), dim3(128), st, op, mp, lp,
-                  lp2, o, lse, ns);
+        return launch(decode_combine_kernel<DT, 64, 4>, dim3((unsigned)((rows + 15) / 16)), dim3(256), st,
+                      op, mp, lp, lp2, o, lse, rows, ns);
+    return launch(decode_combine_kernel<DT, 128, 4>, dim3((unsigned)((rows + 7) / 8)), dim3(256), st, op,
+                  mp, lp, lp2, o, lse, rows, ns);
 }
 
 }  // namespace

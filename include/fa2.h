@@ -217,6 +217,8 @@ fa2_status attn_decode_split(const void *q, const void *k, const void *v,
  *
  *   o_part [B,H,n_splits,D], m_part, l_part [B,H,n_splits] float32 (as written
  *   by attn_decode_split);  o [B,H,D] dtype, rounded to nearest-even.
+ *   Alignment: o_part and o 16 bytes (the general rule); m_part and l_part
+ *   only need 4.
  *   Supported: D in {64, 128}; dtype F16, BF16, F32; n_splits >= 1.
  */
 fa2_status attn_decode_combine(const float *o_part, const float *m_part, const float *l_part,

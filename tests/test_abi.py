@@ -104,6 +104,8 @@ def test_decode_error_paths():
     assert L.attn_decode_combine(ok, ok, ok, None, 1, 1, 128, 4, 1, None) == 1
     assert L.attn_decode_combine(ok, ok, ok, ok, 1, 1, 80, 4, 1, None) == 3
     assert L.attn_decode_combine(ok, ok, ok, ok, 0, 1, 128, 4, 1, None) == 0
+    # o_part is read 16 bytes at a time; m_part and l_part need only 4
+    assert L.attn_decode_combine(ctypes.c_void_p(4100), ok, ok, ok, 1, 1, 128, 4, 1, None) == 4
 
 
 def test_default_splits_host_logic():
