@@ -927,7 +927,7 @@ struct Plan {
                                 // and the keys span at least this many 64-key blocks (0: never)
 #endif
 #ifndef FA2_MFMA_SPLIT_LONG_HALF
-#define FA2_MFMA_SPLIT_LONG_HALF 128  // ... or at most half of the slots and at least this many
+#define FA2_MFMA_SPLIT_LONG_HALF 64  // ... or at most half of the slots and at least this many
                                       // blocks (0: never)
 #endif
 
@@ -961,9 +961,9 @@ Plan plan(int B, int H, int Nq, int Nk, int D, int num_cus) {
         // Long keys with the tiles filling at most a quarter of the resident
         // workgroup slots: cut the keys so the chunks fill the slots (the
         // partials then cost little next to the work of each chunk).  At half
-        // the slots only with very long keys: B4 H12 with 1024 queries split
-        // in two measured 38.6 -> 47.3 us at 2048 keys, no change at 4096,
-        // 140.1 -> 127.3 us at 8192.
+        // the slots only with long keys: B4 H12 with 1024 queries split in
+        // two measured 39.2 -> 43.3 us at 2048 keys, 77.0 -> 72.7 us at 4096
+        // (bf16 with LSE 77.2 -> 70.9), 140.1 -> 125.6 us at 8192.
         const long long slots = (long long)num_cus * (p.qg == 1 && D == 64 ? 3 : 2);
         if (4 * nt <= slots ||
             (FA2_MFMA_SPLIT_LONG_HALF > 0 && nblk >= FA2_MFMA_SPLIT_LONG_HALF && 2 * nt <= slots)) {
