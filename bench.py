@@ -614,7 +614,7 @@ def main():
         },
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_F32,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_F32, 4),
-                     "traffic": traffic.get("fwd_f32"), "kernel": "fwd_f32_rows_kernel<64, false>",
+                     "traffic": traffic.get("fwd_f32"), "kernel": "fwd_f32_rows_kernel<64, false, 2, 2>",
                      "us": round(pre_ms * 1e3, 3), "us_median": round(pre_t[K // 2] * 1e3, 3),
                      "flops_per_launch": pre.flops},
         "accuracy": acc.get(pre.name),

@@ -69,7 +69,7 @@ namespace {
 
 size_t fwd_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, fa2_dtype dtype,
                            int cus) {
-    if (dtype == FA2_F32) return fa2::f32_workspace_bytes(B, H, Nq, Nk, D, cus);
+    if (dtype == FA2_F32) return fa2::f32_workspace_bytes(B, H, Nq, Nk, D, causal, cus);
     return fa2::mfma_workspace_bytes(B, H, Nq, Nk, D, causal, cus);
 }
 

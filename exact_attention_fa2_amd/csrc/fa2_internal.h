@@ -50,7 +50,7 @@ struct FwdArgs {
 
 // float32 forward on float32 matrix cores, D = 64 or 128.
 fa2_status launch_fwd_f32(const FwdArgs &a, hipStream_t st);
-size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int D, int num_cus);
+size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, int num_cus);
 // f16/bf16 forward on matrix cores, D = 64 or 128.
 fa2_status launch_fwd_mfma(const FwdArgs &a, fa2_dtype dt, hipStream_t st);
 size_t mfma_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, int num_cus);

@@ -31,6 +31,9 @@
 // The contraction index of both products is only a pairing of operand slots,
 // so A and B just have to agree on it.
 #include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <random>
 
 #include "fa2_device.h"
 #include "fa2_internal.h"
@@ -58,10 +61,10 @@ constexpr float kLazyCap = 256.f;
 // the last tiles would carry a full unmasked load.  With b*h a multiple of 8,
 // each XCD also sees only every eighth head, and its L2 holds their K and V.
 template <bool CAUSAL>
-__device__ __forceinline__ void tile_of(int n_qtiles, int &qt, int &bh) {
-    const int n_bh = gridDim.x / n_qtiles;
-    qt = blockIdx.x / n_bh;
-    bh = blockIdx.x - qt * n_bh;
+__device__ __forceinline__ void tile_of(int n_qtiles, int index, int count, int &qt, int &bh) {
+    const int n_bh = count / n_qtiles;
+    qt = index / n_bh;
+    bh = index - qt * n_bh;
     if (CAUSAL) qt = n_qtiles - 1 - qt;
 }
 
@@ -70,11 +73,16 @@ inline dim3 tile_grid(long long n_qtiles, long long n_bh, int chunks) {
     return dim3((unsigned)(n_qtiles * n_bh), 1, (unsigned)chunks);
 }
 
-// Waves of the 16-row kernel: at D = 64, 16 (four per SIMD, 128 registers
-// each); at D = 128 the K/V operands double, so 8 (two per SIMD, 256).
-template <int D>
+// Row-tile kernel shapes.  RB blocks of 16 query rows per workgroup, W waves
+// each walking a contiguous slice of the workgroup's keys:
+//   D = 64,  RB = 1: 16 waves (four per SIMD, 128 registers each);
+//   D = 64,  RB = 2: 8 waves (two per SIMD, 164 registers): every K/V operand
+//                    a wave loads feeds both row blocks, so loads per flop and
+//                    the per-step vector work halve;
+//   D = 128, RB = 1: 8 waves (the K/V operands double, 256 registers).
+template <int D, int RB>
 constexpr int rows_waves() {
-    return D == 64 ? 16 : 8;
+    return D == 64 && RB == 1 ? 16 : 8;
 }
 
 template <int D>
@@ -105,75 +113,118 @@ __device__ __forceinline__ void load_kv(KVRegs<D> &r, const float *Kh, const flo
                 f32x4, load16(rv, (uint32_t)(((4 * g + t) * D + 64 * h + 4 * c) * 4)));
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
+// The workgroup's state after its waves are merged, per row: O unnormalised
+// (kD floats), then m (base 2) and l -- one workgroup's share of the keys,
+// written for the workgroup that merges the key chunks of a tile.
+template <int QT, int D>
+constexpr int part_floats() {
+    return QT * D + 2 * QT;
+}
+
+// Row-tile kernel.  A workgroup owns RB * 16 query rows and one of NCH
+// contiguous chunks of their keys; its W waves split that chunk.  With
+// NCH = 2 ("Flash decoding": split the keys, keep unnormalised partials,
+// merge them with the (m, l) monoid of "Flash Attention"), the two
+// workgroups of a tile meet at the end without waiting for each other: each
+// writes its partial state to `part`, then swaps `tag` (a 64-bit value drawn
+// for this launch) into the tile's handshake word; the one that gets `tag`
+// back is second, merges both states and writes O and LSE, and sets the word
+// to 0 again.  The partial state goes through device-scope stores and loads
+// (written through to, and read from, the point where all XCDs' caches
+// agree) so neither side needs a cache-wide write-back or invalidate; the
+// swap is issued only after those stores have completed.
+template <int D, bool CAUSAL, int RB, int NCH>
+__global__ __launch_bounds__((rows_waves<D, RB>() * 64), 1) void fwd_f32_rows_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
-    float *__restrict__ O, float *__restrict__ LSE, int Nq, int Nk, float scale_log2) {
-    constexpr int W = rows_waves<D>();
+    float *__restrict__ O, float *__restrict__ LSE, int Nq, int Nk, float scale_log2,
+    float *__restrict__ part, unsigned long long *__restrict__ tags, unsigned long long tag) {
+    constexpr int W = rows_waves<D, RB>();
     constexpr int NH = D / 64;  // 64-column halves of O
-    __shared__ __attribute__((aligned(16))) float s_o[W][kQT][D];
-    __shared__ float s_m[W][kQT];
-    __shared__ float s_l[W][kQT];
+    constexpr int QT = kQT * RB;  // query rows of the workgroup
+    // score accumulation chains per row block: with one block, two
+    // independent chains (summed at the end) keep the matrix core busy
+    constexpr int NCHAIN = RB == 1 ? 2 : 1;
+    static_assert(NCH == 1 || (D == 64 && QT * D / 4 == W * 64), "the chunk merge maps one f32x4 per thread");
+    __shared__ __attribute__((aligned(16))) float s_o[W][QT][D];
+    __shared__ float s_m[W][QT];
+    __shared__ float s_l[W][QT];
+    __shared__ float s_mg[QT], s_lg[QT];  // the workgroup's merged m and l (chunked launches)
+    __shared__ int s_second;
 
     const int lane = threadIdx.x & 63;
     // wave index as a wave-uniform value, so the key loop below is scalar
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, c = lane & 15;
+    const int n_qtiles = (Nq + QT - 1) / QT;
+    const int unit = blockIdx.x / NCH, chunk = blockIdx.x - unit * NCH;
     int qt, bh;
-    tile_of<CAUSAL>((Nq + kQT - 1) / kQT, qt, bh);
-    const int q0 = qt * kQT;
+    tile_of<CAUSAL>(n_qtiles, unit, gridDim.x / NCH, qt, bh);
+    const int q0 = qt * QT;
 
     const float *Qh = Q + (size_t)bh * Nq * D;
     const float *Kh = K + (size_t)bh * Nk * D;
     const float *Vh = V + (size_t)bh * Nk * D;
     const auto rq = make_rsrc(Qh, (uint32_t)Nq * D * 4);
 
-    // Q^T operand of S^T = K Q^T: slot i of lane (g,c) is Q[q0 + c][d(g,i)]
-    // with d(g,i) = 16*(i/4) + 4g + i%4 -- any pairing of the contraction index
-    // works, and this one lets the four lanes of a key row read 64 contiguous
-    // bytes of K per load instruction.
+    // Q^T operand of S^T = K Q^T: slot i of lane (g,c) in row block b is
+    // Q[q0 + 16b + c][d(g,i)] with d(g,i) = 16*(i/4) + 4g + i%4 -- any pairing
+    // of the contraction index works, and this one lets the four lanes of a
+    // key row read 64 contiguous bytes of K per load instruction.
     // The row maxima below are taken on unscaled scores, which needs a
     // positive scale: a negative one moves onto Q (an exact sign flip) and a
     // zero one becomes Q = 0 with scale 1 (the scaled scores are the same).
     const float qmul = scale_log2 < 0.f ? -1.f : scale_log2 == 0.f ? 0.f : 1.f;
     scale_log2 = scale_log2 == 0.f ? 1.f : fabsf(scale_log2);
 
-    const int kend = CAUSAL ? min(Nk, q0 + kQT) : Nk;
+    // This workgroup's keys: chunk `chunk` of the tile's steps; then this
+    // wave's contiguous share of them (possibly none).
+    const int kend = CAUSAL ? min(Nk, q0 + QT) : Nk;
     const int nsteps = (kend + kStep - 1) / kStep;
-    const int per = (nsteps + W - 1) / W;
-    const int st0 = wave * per;
-    const int st1 = min(nsteps, st0 + per);
+    const int csteps = (nsteps + NCH - 1) / NCH;
+    const int cs0 = min(nsteps, chunk * csteps);
+    const int cs1 = min(nsteps, cs0 + csteps);
+    const int per = (cs1 - cs0 + W - 1) / W;
+    const int st0 = cs0 + wave * per;
+    const int st1 = min(cs1, st0 + per);
 
     // This wave's first K/V operands go out before Q, the larger load first.
     KVRegs<D> ra, rb;
     load_kv<D>(ra, Kh, Vh, Nk, st0 * kStep, g, c);
 
-    // The workgroup's Q tile (16 rows) is read from memory once, through the
-    // merge area of LDS (free until the end), instead of once per wave.
+    // The workgroup's Q tile is read from memory once, through the merge area
+    // of LDS (free until the end), instead of once per wave.
     {
         float *sq = &s_o[0][0][0];
-        for (int e = threadIdx.x; e < kQT * D / 4; e += W * 64)
+        for (int e = threadIdx.x; e < QT * D / 4; e += W * 64)
             *reinterpret_cast<f32x4 *>(sq + 4 * e) = __builtin_bit_cast(f32x4, load16(rq, (uint32_t)((q0 * D + 4 * e) * 4)));
         __syncthreads();
     }
-    float qv[D / 4];
+    float qv[RB][D / 4];
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-        const f32x4 t = *reinterpret_cast<const f32x4 *>(&s_o[0][0][0] + c * D + 16 * j + 4 * g);
-        qv[4 * j + 0] = t[0] * qmul;
-        qv[4 * j + 1] = t[1] * qmul;
-        qv[4 * j + 2] = t[2] * qmul;
-        qv[4 * j + 3] = t[3] * qmul;
-    }
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(&s_o[0][0][0] + (16 * b + c) * D + 16 * j + 4 * g);
+            qv[b][4 * j + 0] = t[0] * qmul;
+            qv[b][4 * j + 1] = t[1] * qmul;
+            qv[b][4 * j + 2] = t[2] * qmul;
+            qv[b][4 * j + 3] = t[3] * qmul;
+        }
     // every wave has its Q before the merge area is written again
     __syncthreads();
 
-    float m = -INFINITY;  // running max of scaled scores, base-2 units
-    float mu = 0.f;       // m, or 0 while the row has no live key yet
-    float l = 0.f;        // this lane's share of the running denominator
-    f32x4 acc[4 * NH];
+    float m[RB], mu[RB], l[RB];  // per row block: running max of scaled scores
+                                 // (base 2), that max or 0 while the row has no
+                                 // live key yet, this lane's share of l
+    f32x4 acc[RB][4 * NH];
 #pragma unroll
-    for (int j = 0; j < 4 * NH; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < RB; ++b) {
+        m[b] = -INFINITY;
+        mu[b] = 0.f;
+        l[b] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4 * NH; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // One 16-key step on the registers in `cur`; the next step's K/V are
     // loaded into `nxt` first so the loads overlap this step's work.  The load
@@ -188,66 +239,89 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
         // their use in the following step, which serialises load and compute
         __builtin_amdgcn_sched_barrier(0);
 
-        // two independent accumulation chains, summed at the end
-        f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, sacc2 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 sacc[RB][NCHAIN];
 #pragma unroll
-        for (int i = 0; i < D / 4; i += 2) {
-            sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.k[i >> 2][i & 3], qv[i], sacc, 0, 0, 0);
-            sacc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.k[i >> 2][(i & 3) + 1], qv[i + 1], sacc2,
-                                                        0, 0, 0);
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+            for (int ch = 0; ch < NCHAIN; ++ch) sacc[b][ch] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < D / 4; i += NCHAIN)
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+#pragma unroll
+                for (int ch = 0; ch < NCHAIN; ++ch)
+                    sacc[b][ch] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.k[(i + ch) >> 2][(i + ch) & 3],
+                                                                      qv[b][i + ch], sacc[b][ch], 0, 0, 0);
+        if constexpr (NCHAIN == 2) {
+#pragma unroll
+            for (int b = 0; b < RB; ++b) sacc[b][0] += sacc[b][1];
         }
-        sacc += sacc2;
 
-        // sacc[r] = S[query q0 + c][key k0 + 4g + r] (unscaled); a step past
-        // this wave's slice is masked entirely and leaves the state unchanged.
-        // Only steps that reach past Nk, cross the causal diagonal or lie past
-        // the slice need the per-score mask (a wave-uniform test).
-        float s[4];
+        // sacc[b][0][r] = S[query q0 + 16b + c][key k0 + 4g + r] (unscaled); a
+        // step past this wave's slice is masked entirely and leaves the state
+        // unchanged.  Only steps that reach past Nk, cross the causal diagonal
+        // or lie past the slice need the per-score mask (a wave-uniform test).
+        float s[RB][4];
         const bool in_slice = st < st1;
         if (in_slice && k0 + kStep <= Nk && !(CAUSAL && k0 + kStep - 1 > q0)) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s[r] = sacc[r];
+            for (int b = 0; b < RB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s[b][r] = sacc[b][0][r];
         } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = k0 + 4 * g + r;
-                bool live = in_slice && key < Nk;
-                if (CAUSAL) live = live && key <= q0 + c;
-                s[r] = live ? sacc[r] : -INFINITY;
-            }
-        }
-        float p[4];
+            for (int b = 0; b < RB; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = exp2f_fast(__builtin_fmaf(s[r], scale_log2, -mu));
-        float psum = (p[0] + p[1]) + (p[2] + p[3]);
+                for (int r = 0; r < 4; ++r) {
+                    const int key = k0 + 4 * g + r;
+                    bool live = in_slice && key < Nk;
+                    if (CAUSAL) live = live && key <= q0 + 16 * b + c;
+                    s[b][r] = live ? sacc[b][0][r] : -INFINITY;
+                }
+        }
+        float p[RB][4], psum[RB];
+        bool need = false;
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[b][r] = exp2f_fast(__builtin_fmaf(s[b][r], scale_log2, -mu[b]));
+            psum[b] = (p[b][0] + p[b][1]) + (p[b][2] + p[b][3]);
+            need = need || m[b] == -INFINITY || psum[b] > kLazyCap;
+        }
         // The max is only taken (and O rescaled) when a row has none yet or a
         // score has overtaken it far enough to push some P past the cap; a
         // rescale by exactly 1 would change nothing.
-        if (__builtin_amdgcn_ballot_w64(m == -INFINITY || psum > kLazyCap) != 0) {
-            float mx = fmax_nan(fmax_nan(s[0], s[1]), fmax_nan(s[2], s[3]));
-            mx = max_xor32(max_xor16(mx)) * scale_log2;  // base-2 units of the scaled scores
-            const float m_new = fmax_nan(m, mx);
-            mu = m_new == -INFINITY ? 0.f : m_new;
-            const float corr = exp2f_fast(m - mu);
-            l *= corr;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
-            for (int j = 0; j < 4 * NH; ++j) acc[j] *= corr;
-            m = m_new;
+            for (int b = 0; b < RB; ++b) {
+                float mx = fmax_nan(fmax_nan(s[b][0], s[b][1]), fmax_nan(s[b][2], s[b][3]));
+                mx = max_xor32(max_xor16(mx)) * scale_log2;  // base-2 units of the scaled scores
+                const float m_new = fmax_nan(m[b], mx);
+                mu[b] = m_new == -INFINITY ? 0.f : m_new;
+                const float corr = exp2f_fast(m[b] - mu[b]);
+                l[b] *= corr;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = exp2f_fast(__builtin_fmaf(s[r], scale_log2, -mu));
-            psum = (p[0] + p[1]) + (p[2] + p[3]);
+                for (int j = 0; j < 4 * NH; ++j) acc[b][j] *= corr;
+                m[b] = m_new;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p[b][r] = exp2f_fast(__builtin_fmaf(s[b][r], scale_log2, -mu[b]));
+                psum[b] = (p[b][0] + p[b][1]) + (p[b][2] + p[b][3]);
+            }
         }
-        l += psum;
+#pragma unroll
+        for (int b = 0; b < RB; ++b) l[b] += psum[b];
         // O^T += V^T P^T: slot g pairs key k0 + 4g + t; row m of tile 4h + j is
         // d = 64h + 4m + j.
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int h = 0; h < NH; ++h)
+            for (int b = 0; b < RB; ++b)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[4 * h + j] =
-                        __builtin_amdgcn_mfma_f32_16x16x4f32(cur.v[t][h][j], p[t], acc[4 * h + j], 0, 0, 0);
+                for (int h = 0; h < NH; ++h)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[b][4 * h + j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            cur.v[t][h][j], p[b][t], acc[b][4 * h + j], 0, 0, 0);
     };
 
     // Steps run in pairs, unconditionally, so each step's prefetch has a
@@ -257,29 +331,34 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
         step(st + 1, rb, ra);
     }
 
-    // acc[4h + j][r] = O[q0 + c][64h + 16g + 4r + j]; the lane's l covers keys
-    // 4g..4g+3 of each step.
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (g == 0) {
-        s_m[wave][c] = m;
-        s_l[wave][c] = l;
+    // acc[b][4h + j][r] = O[q0 + 16b + c][64h + 16g + 4r + j]; the lane's l
+    // covers keys 4g..4g+3 of each step.
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+        float lb = l[b];
+        lb += __shfl_xor(lb, 16);
+        lb += __shfl_xor(lb, 32);
+        if (g == 0) {
+            s_m[wave][16 * b + c] = m[b];
+            s_l[wave][16 * b + c] = lb;
+        }
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<f32x4 *>(&s_o[wave][16 * b + c][64 * h + 16 * g + 4 * r]) =
+                    f32x4{acc[b][4 * h][r], acc[b][4 * h + 1][r], acc[b][4 * h + 2][r], acc[b][4 * h + 3][r]};
     }
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            *reinterpret_cast<f32x4 *>(&s_o[wave][c][64 * h + 16 * g + 4 * r]) =
-                f32x4{acc[4 * h][r], acc[4 * h + 1][r], acc[4 * h + 2][r], acc[4 * h + 3][r]};
     __syncthreads();
 
     // Merge the wave states of each row ((m, l) merge of the online softmax).
     // First W lanes per row, one per wave state: the row's max m by a
     // reduction over those lanes, each state's weight 2^(m_w - m), and l as
     // the weighted sum of the states' l.  The weights replace the row's s_m
-    // entries and s_l[0][row] holds 1 / l (each row's lanes sit in one wave and
-    // read their entries before any of them is written).
-    if (threadIdx.x < kQT * W) {
+    // entries; the row's m and l go to s_mg, s_lg, and s_l[0][row] holds 1 / l
+    // (each row's lanes sit in one wave and read their entries before any of
+    // them is written).
+    if (threadIdx.x < QT * W) {
         const int row = threadIdx.x / W, w = threadIdx.x % W;
         const float mw = s_m[w][row];
         const float mg = group_reduce<W, true>(mw);
@@ -287,22 +366,75 @@ __global__ __launch_bounds__(rows_waves<D>() * 64, 1) void fwd_f32_rows_kernel(
         const float lg = group_reduce<W>(wt * s_l[w][row]);
         s_m[w][row] = wt;
         if (w == 0) {
+            s_mg[row] = mg;
+            s_lg[row] = lg;
             s_l[0][row] = 1.f / lg;
             const int qrow = q0 + row;
-            if (LSE && qrow < Nq) LSE[(size_t)bh * Nq + qrow] = (mg + log2f_fast(lg)) * kLn2;
+            if (NCH == 1 && LSE && qrow < Nq) LSE[(size_t)bh * Nq + qrow] = (mg + log2f_fast(lg)) * kLn2;
         }
     }
     __syncthreads();
-    // Then four consecutive output columns per thread: the weighted sum of
-    // the states' O, divided by l once.
-    for (int e = threadIdx.x; e < kQT * D / 4; e += W * 64) {
-        const int row = e / (D / 4);
-        const int d = 4 * (e % (D / 4));
+    if constexpr (NCH == 1) {
+        // Four consecutive output columns per thread: the weighted sum of the
+        // states' O, divided by l once.
+        for (int e = threadIdx.x; e < QT * D / 4; e += W * 64) {
+            const int row = e / (D / 4);
+            const int d = 4 * (e % (D / 4));
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < W; ++w) o += s_m[w][row] * *reinterpret_cast<const f32x4 *>(&s_o[w][row][d]);
+            const int qrow = q0 + row;
+            if (qrow < Nq) *reinterpret_cast<f32x4 *>(O + ((size_t)bh * Nq + qrow) * D + d) = o * s_l[0][row];
+        }
+    } else {
+        // One f32x4 of the workgroup's unnormalised O per thread.
+        const int row = threadIdx.x / (D / 4);
+        const int d = 4 * (threadIdx.x % (D / 4));
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < W; ++w) o += s_m[w][row] * *reinterpret_cast<const f32x4 *>(&s_o[w][row][d]);
+
+        // Publish this chunk's state (cache policy 16 = device scope), wait
+        // until every store of the workgroup has completed, then swap the tag.
+        constexpr int kDev = 16;
+        constexpr int PF = part_floats<QT, D>();
+        const auto rmine = make_rsrc(part + ((size_t)unit * NCH + chunk) * PF, PF * 4);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rmine, (row * D + d) * 4, 0, kDev);
+        if (d == 0) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_mg[row]), rmine, (QT * D + row) * 4, 0, kDev);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_lg[row]), rmine, (QT * D + QT + row) * 4, 0, kDev);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned long long old = atomicExch(&tags[unit], tag);
+            const int second = old == tag;
+            if (second) atomicExch(&tags[unit], 0ull);  // ready for the next launch
+            s_second = second;
+        }
+        __syncthreads();
+        if (!s_second) return;
+
+        // Second: merge the two chunks' states in chunk order (the same
+        // arithmetic whichever workgroup does it) and write O and LSE.
+        const auto rother = make_rsrc(part + ((size_t)unit * NCH + (chunk ^ 1)) * PF, PF * 4);
+        const f32x4 oo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rother, (row * D + d) * 4, 0, kDev));
+        const float mo = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rother, (QT * D + row) * 4, 0, kDev));
+        const float lo = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rother, (QT * D + QT + row) * 4, 0, kDev));
+        const float mm = s_mg[row], lm = s_lg[row];
+        const bool c0 = chunk == 0;
+        const float m0 = c0 ? mm : mo, m1 = c0 ? mo : mm;
+        const float l0 = c0 ? lm : lo, l1 = c0 ? lo : lm;
+        const f32x4 o0 = c0 ? o : oo, o1 = c0 ? oo : o;
+        const float mg = fmax_nan(m0, m1);
+        const float w0 = m0 == -INFINITY ? 0.f : exp2f_fast(m0 - mg);
+        const float w1 = m1 == -INFINITY ? 0.f : exp2f_fast(m1 - mg);
+        const float lg = w0 * l0 + w1 * l1;
         const int qrow = q0 + row;
-        if (qrow < Nq) *reinterpret_cast<f32x4 *>(O + ((size_t)bh * Nq + qrow) * D + d) = o * s_l[0][row];
+        if (qrow < Nq) {
+            *reinterpret_cast<f32x4 *>(O + ((size_t)bh * Nq + qrow) * D + d) = (w0 * o0 + w1 * o1) * (1.f / lg);
+            if (LSE && d == 0) LSE[(size_t)bh * Nq + qrow] = (mg + log2f_fast(lg)) * kLn2;
+        }
     }
 }
 
@@ -345,7 +477,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void kernel(
     const int ss = wave / kTiles;        // key sub-slice of this wave
     const int g = lane >> 4, c = lane & 15;
     int qt, bh;
-    tile_of<CAUSAL>((Nq + kRows - 1) / kRows, qt, bh);
+    tile_of<CAUSAL>((Nq + kRows - 1) / kRows, blockIdx.x, gridDim.x, qt, bh);
     const int q0 = qt * kRows;
     const int chunk = blockIdx.z, nchunks = gridDim.z;
     const int qt0 = q0 + qa * kQT;  // first row of this wave's tile
@@ -570,6 +702,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void kernel(
 #ifndef FA2_F32_SPLIT_WAVES
 #define FA2_F32_SPLIT_WAVES 1  // chunks so that groups x chunks = this many per compute unit
 #endif
+// 1: D = 64 shapes with at least one 64-row group per compute unit run the
+// shared-K/V kernel; 0: they run the row-tile kernels.
+#ifndef FA2_F32_SHARED
+#define FA2_F32_SHARED 1
+#endif
+// 1: unmasked D = 64 shapes with too few 64-row groups for the shared kernel
+// run the 32-row kernel (its keys split in two and merged in the kernel when
+// the 32-row tiles cover only half the device); 0: the 16-row kernel.
+#ifndef FA2_F32_ROWS32
+#define FA2_F32_ROWS32 1
+#endif
 
 int f32_chunks(int B, int H, int Nq, int Nk, int num_cus) {
     const long long groups = (long long)B * H * ((Nq + shared::kRows - 1) / shared::kRows);
@@ -582,24 +725,105 @@ int f32_chunks(int B, int H, int Nq, int Nk, int num_cus) {
     return (int)std::max<long long>(1, c);
 }
 
-size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int D, int num_cus) {
-    if (D != kD) return 0;  // D = 128 always runs the 16-row kernel
-    const int c = f32_chunks(B, H, Nq, Nk, num_cus);
-    if (c <= 1) return 0;
-    return (size_t)B * H * Nq * c * (kD + 2) * sizeof(float);
+namespace {
+
+constexpr int kRows32 = 2 * kQT;  // query rows of the 32-row kernel's workgroup
+
+// Which D = 64 kernel a shape gets.
+enum class F32Plan { Shared, Rows32, Rows32Split, SharedSplit, Rows16 };
+
+// Unmasked shapes whose 32-row tiles, split in two, cover the device take
+// whichever row-tile schedule should finish first.  Workgroups run in rounds
+// of one per compute unit, so a schedule costs its rounds times the time of
+// one workgroup, counted per SIMD in steps of 16 keys for 16 rows:
+//   16-row tiles:       4 waves x ceil(n / 16) steps
+//   32-row tiles:       2 waves x ceil(n / 8) steps x 2 blocks x 0.9
+//   32-row, keys split: 2 waves x ceil(ceil(n / 2) / 8) steps x 2 x 0.9 + 3
+// (n = steps of the keys; a 32-row step takes 0.9 of two 16-row steps,
+// measured on one head of 4096 x 4096: 36.5 against 40.3 us per launch
+// before the merge; the merge of a split tile costs about 3 steps, 1.8 us).
+// This picked the faster schedule on every shape measured, and the 32-row
+// kernel also beat the shared-K/V kernel on every many-row shape (by 3-21%).
+// Causal shapes keep the 16-row and shared-K/V kernels: their tiles differ
+// in length, and with 32-row tiles the longest ones set the time (single
+// head of 8192, causal: 127 against 88 us).  So do shapes with fewer rows,
+// which split the keys across 64-row groups and merge with the combine.
+F32Plan f32_plan(int B, int H, int Nq, int Nk, int causal, int num_cus, bool have_ws) {
+    const long long bh = (long long)B * H;
+    const long long groups = bh * ((Nq + shared::kRows - 1) / shared::kRows);
+    const long long t16 = bh * ((Nq + kQT - 1) / kQT);
+    const long long t32 = bh * ((Nq + kRows32 - 1) / kRows32);
+    if (FA2_F32_ROWS32 && !causal && 2 * t32 >= num_cus) {
+        auto rounds = [&](long long wgs) { return (double)((wgs + num_cus - 1) / num_cus); };
+        const long long n = (Nk + kStep - 1) / kStep;
+        const double c16 = rounds(t16) * 4.0 * ((n + 15) / 16);
+        const double c32 = rounds(t32) * 3.6 * ((n + 7) / 8);
+        const double c32s = rounds(2 * t32) * (3.6 * (((n + 1) / 2 + 7) / 8) + 3.0);
+        if (have_ws && c32s < c32 && c32s < c16) return F32Plan::Rows32Split;
+        return c32 < c16 ? F32Plan::Rows32 : F32Plan::Rows16;
+    }
+    if (FA2_F32_SHARED && groups >= num_cus) return F32Plan::Shared;
+    return f32_chunks(B, H, Nq, Nk, num_cus) > 1 ? F32Plan::SharedSplit : F32Plan::Rows16;
 }
 
-#ifndef FA2_F32_SHARED
-#define FA2_F32_SHARED 1
-#endif
+// Workspace of the 32-row kernel with its keys split in two: a 64-bit
+// handshake word per tile, then two partial states per tile.
+size_t rows32_split_bytes(long long tiles) {
+    const size_t words = ((size_t)tiles * 8 + 255) / 256 * 256;
+    return words + (size_t)tiles * 2 * part_floats<kRows32, kD>() * sizeof(float);
+}
 
-template <int D>
-fa2_status launch_rows(const FwdArgs &a, float sl2, hipStream_t st) {
-    const dim3 grid = tile_grid((a.Nq + kQT - 1) / kQT, a.B * a.H, 1);
-    const dim3 block(rows_waves<D>() * 64);
-    auto k = a.causal ? fwd_f32_rows_kernel<D, true> : fwd_f32_rows_kernel<D, false>;
-    return launch(k, grid, block, st, (const float *)a.q, (const float *)a.k, (const float *)a.v,
-                  (float *)a.o, a.lse, a.Nq, a.Nk, sl2);
+// A fresh 64-bit value per launch for the handshake words: a counter with a
+// random start, stepped by the golden-ratio increment and scrambled by the
+// SplitMix64 finaliser (Steele, Lea and Flood, "Fast splittable pseudorandom
+// number generators", 2014); forced odd, so never 0 (a word's resting value).
+unsigned long long next_tag() {
+    static std::atomic<unsigned long long> state{[] {
+        std::random_device rd;
+        return ((unsigned long long)rd() << 32) ^ rd() ^
+               (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    }()};
+    unsigned long long z = state.fetch_add(0x9E3779B97F4A7C15ull) + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return (z ^ (z >> 31)) | 1ull;
+}
+
+}  // namespace
+
+size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, int num_cus) {
+    if (D != kD) return 0;  // D = 128 always runs the 16-row kernel
+    switch (f32_plan(B, H, Nq, Nk, causal, num_cus, true)) {
+        case F32Plan::Rows32Split:
+            return rows32_split_bytes((long long)B * H * ((Nq + kRows32 - 1) / kRows32));
+        case F32Plan::SharedSplit: {
+            const int c = f32_chunks(B, H, Nq, Nk, num_cus);
+            return (size_t)B * H * Nq * c * (kD + 2) * sizeof(float);
+        }
+        default:
+            return 0;
+    }
+}
+
+// The row-tile kernel on a one-dimensional grid of NCH workgroups per tile
+// (chunk fastest), b*h next, query tile slowest.
+template <int D, int RB, int NCH>
+fa2_status launch_rows(const FwdArgs &a, float sl2, hipStream_t st, float *part = nullptr,
+                       unsigned long long *tags = nullptr, unsigned long long tag = 0) {
+    constexpr int QT = kQT * RB;
+    const long long units = (long long)((a.Nq + QT - 1) / QT) * a.B * a.H;
+    const dim3 grid((unsigned)(units * NCH));
+    const dim3 block(rows_waves<D, RB>() * 64);
+    if constexpr (RB == 1) {
+        auto k = a.causal ? fwd_f32_rows_kernel<D, true, 1, NCH> : fwd_f32_rows_kernel<D, false, 1, NCH>;
+        return launch(k, grid, block, st, (const float *)a.q, (const float *)a.k, (const float *)a.v,
+                      (float *)a.o, a.lse, a.Nq, a.Nk, sl2, part, tags, tag);
+    } else {
+        if (a.causal) return FA2_ERR_UNSUPPORTED;  // the planner sends only unmasked shapes here
+        return launch(fwd_f32_rows_kernel<D, false, RB, NCH>, grid, block, st, (const float *)a.q,
+                      (const float *)a.k, (const float *)a.v,
+                      (float *)a.o, a.lse, a.Nq, a.Nk, sl2, part, tags, tag);
+    }
 }
 
 fa2_status launch_fwd_f32(const FwdArgs &a, hipStream_t st) {
@@ -609,10 +833,12 @@ fa2_status launch_fwd_f32(const FwdArgs &a, hipStream_t st) {
     // D = 128: the 16-row kernel at two waves per SIMD for every shape (the
     // shared-K/V kernel holds the operands of four query tiles per wave group
     // and has no registers for twice the columns)
-    if (a.D == 128) return launch_rows<128>(a, sl2, st);
-    const long long groups = (long long)a.B * a.H * ((a.Nq + shared::kRows - 1) / shared::kRows);
+    if (a.D == 128) return launch_rows<128, 1, 1>(a, sl2, st);
     const dim3 block(kWaves * 64);
-    if (FA2_F32_SHARED && groups >= a.num_cus) {
+    const size_t need = f32_workspace_bytes(a.B, a.H, a.Nq, a.Nk, kD, a.causal, a.num_cus);
+    const bool ws_ok = need > 0 && a.ws && a.ws_bytes >= need;
+    const F32Plan plan = f32_plan(a.B, a.H, a.Nq, a.Nk, a.causal, a.num_cus, ws_ok);
+    if (plan == F32Plan::Shared) {
         // enough 64-row groups to fill the device: share K/V, no split
         const dim3 grid = tile_grid((a.Nq + shared::kRows - 1) / shared::kRows, a.B * a.H, 1);
         auto k = a.causal ? shared::kernel<true, false> : shared::kernel<false, false>;
@@ -620,9 +846,18 @@ fa2_status launch_fwd_f32(const FwdArgs &a, hipStream_t st) {
                       (float *)a.o, a.lse, (float *)nullptr, (float *)nullptr, (float *)nullptr,
                       a.Nq, a.Nk, sl2);
     }
-    const int c = f32_chunks(a.B, a.H, a.Nq, a.Nk, a.num_cus);
-    if (c > 1 && a.ws && a.ws_bytes >= f32_workspace_bytes(a.B, a.H, a.Nq, a.Nk, kD, a.num_cus)) {
+    if (plan == F32Plan::Rows32) return launch_rows<kD, 2, 1>(a, sl2, st);
+    if (plan == F32Plan::Rows32Split) {
+        // each 32-row tile's keys in two chunks, merged by the second of its
+        // two workgroups
+        const long long tiles = (long long)a.B * a.H * ((a.Nq + kRows32 - 1) / kRows32);
+        auto *tags = (unsigned long long *)a.ws;
+        float *part = (float *)((char *)a.ws + (need - (size_t)tiles * 2 * part_floats<kRows32, kD>() * sizeof(float)));
+        return launch_rows<kD, 2, 2>(a, sl2, st, part, tags, next_tag());
+    }
+    if (plan == F32Plan::SharedSplit && ws_ok) {
         // few rows: split the keys into c chunks, then merge the partials
+        const int c = f32_chunks(a.B, a.H, a.Nq, a.Nk, a.num_cus);
         const size_t rows = (size_t)a.B * a.H * a.Nq;
         float *o_part = (float *)a.ws;
         float *m_part = o_part + rows * c * kD;
@@ -636,7 +871,7 @@ fa2_status launch_fwd_f32(const FwdArgs &a, hipStream_t st) {
         return launch_combine_rows(o_part, m_part, l_part, a.o, a.lse, rows, kD, c, FA2_F32, st);
     }
     // few rows and no workspace: 16-row workgroups fill the device instead
-    return launch_rows<kD>(a, sl2, st);
+    return launch_rows<kD, 1, 1>(a, sl2, st);
 }
 
 }  // namespace fa2

@@ -102,8 +102,17 @@ fa2_status attn_fwd(const void *q, const void *k, const void *v, void *o, float 
  * smaller workspace it runs exactly as attn_fwd.  The two paths may differ in
  * the last bits (the sums are grouped differently), each within the bounds
  * stated for attn_fwd.
- *   workspace  device memory, 16-byte aligned, owned by the caller; its
- *              contents on entry are ignored and on return are unspecified.
+ *   For unmasked float32 D = 64 shapes with few 32-row query tiles, the split
+ *   is instead two key chunks per tile, whose workgroups meet at the end with
+ *   no wait: each publishes its partial state, then swaps a 64-bit value drawn
+ *   for this call into the tile's handshake word in the workspace; the one
+ *   that gets the value back merges and writes o and lse, and resets the word.
+ *   workspace  device memory, 16-byte aligned, owned by the caller.  Its
+ *              contents on entry do not matter: the handshake words are read
+ *              before they are written, but only a word that already holds
+ *              this call's value (odd; a counter with a random start,
+ *              scrambled by the SplitMix64 finaliser) would count, and every
+ *              call leaves them 0.  On return the rest is unspecified.
  *              Calls that share one workspace must not overlap in time.
  */
 fa2_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -129,7 +138,9 @@ fa2_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, flo
  *            keeps the last call's contents: calls that can overlap in time on
  *            one device (different streams, or different host threads) race.
  *            Serialise them, e.g. issue them on one stream.  The array's
- *            contents on entry are never read before they are written.
+ *            contents on entry do not change the result (see attn_fwd_ws:
+ *            the only words read before they are written are handshake
+ *            words, compared with a value drawn for each call).
  */
 #define FA2_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 fa2_status attn_fwd_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,

@@ -300,6 +300,60 @@ def test_f32_schedules(shape, causal):
         assert_close("f32 schedule %s LSE" % tag, download_f64(lse), rl, LSE_TOL)
 
 
+# Unmasked float32 D = 64 shapes whose 32-row tiles, split in two, cover the
+# device run 32-row workgroups, or 16-row ones where those should finish
+# first; where the key split should finish first (split = True, on 256
+# compute units) each tile's keys go to two workgroups whose states are
+# merged by the second to finish.
+ROWS32_SHAPES = [(1, 1, 4090, 4096, True),   # ragged last tile
+                 (1, 1, 4096, 4000, True),   # ragged keys
+                 (1, 2, 2040, 3333, True),
+                 (1, 4, 1000, 4000, True),
+                 (3, 1, 3000, 2000, True),   # 282 tiles of 32 rows: the split takes the fewest rounds
+                 (1, 1, 4096, 16, False),    # one or two key steps: 32-row tiles, no split
+                 (1, 1, 4096, 17, False),
+                 (1, 1, 4096, 1, False),
+                 (1, 2, 4096, 4096, False),  # 256 tiles of 32 rows
+                 (2, 12, 1024, 1024, False)]
+
+
+@pytest.mark.parametrize("shape", ROWS32_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_rows32(shape):
+    """The 32-row float32 kernel, O and LSE against the oracle.  With the key
+    split, the workspace starts out as random bytes (the handshake words'
+    earlier contents must not matter), every call must leave those words at 0,
+    the same call twice must give the same bits, and a call on other values
+    with the same workspace must match the oracle again (no state carried
+    over).  Without a workspace the shape runs the 16-row kernel."""
+    import torch
+    B, H, Nq, Nk, split = shape
+    need = fa2.workspace_size(B, H, Nq, Nk, 64, False, fa2.FA2_F32)
+    assert (need > 0) == split, "the shape takes another schedule (need=%d)" % need
+    tiles = B * H * ((Nq + 31) // 32)
+    ws = torch.randint(0, 256, (max(need, 1),), dtype=torch.uint8, device="cuda")
+    first = None
+    for seed in (16, 16, 17):
+        q, k, v = seeded(B, H, Nq, Nk, 64, "f32", seed)
+        ro, rl = oracle.attn(*(inputs.to_f64(x, "f32") for x in (q, k, v)), 0.125, False)
+        tq, tk, tv = upload(q, "f32"), upload(k, "f32"), upload(v, "f32")
+        o, lse = fa2.attn_fwd(tq, tk, tv, scale=0.125, return_lse=True, workspace=ws)
+        torch.cuda.synchronize()
+        tag = "rows32 seed %d split=%d" % (seed, split)
+        assert_close(tag + " O", download_f64(o), ro, TOL["f32"])
+        assert_close(tag + " LSE", download_f64(lse), rl, LSE_TOL)
+        if split:
+            words = ws[:8 * tiles].cpu().numpy()
+            assert not words.any(), "handshake words left set after the call"
+        if first is None:
+            first = (o.clone(), lse.clone())
+        elif seed == 16:
+            assert torch.equal(o, first[0]) and torch.equal(lse, first[1]), "not deterministic"
+    o, lse = fa2.attn_fwd(tq, tk, tv, scale=0.125, return_lse=True, use_workspace=False)
+    torch.cuda.synchronize()
+    assert_close("rows32 shape without workspace O", download_f64(o), ro, TOL["f32"])
+    assert_close("rows32 shape without workspace LSE", download_f64(lse), rl, LSE_TOL)
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", [(1, 2, 1024, 1024, True), (1, 2, 1024, 1024, False),
                                    (1, 1, 700, 700, True), (2, 3, 300, 300, False),
