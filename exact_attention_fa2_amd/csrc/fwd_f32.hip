@@ -742,6 +742,8 @@ enum class F32Plan { Shared, Rows32, Rows32Split, SharedSplit, Rows16 };
 // (n = steps of the keys; a 32-row step takes 0.9 of two 16-row steps,
 // measured on one head of 4096 x 4096: 36.5 against 40.3 us per launch
 // before the merge; the merge of a split tile costs about 3 steps, 1.8 us).
+// The split is taken only when it should save at least 3% (below that the
+// model cannot tell, and the split needs a workspace of 16.5 KB per tile).
 // This picked the faster schedule on every shape measured, and the 32-row
 // kernel also beat the shared-K/V kernel on every many-row shape (by 3-21%).
 // Causal shapes keep the 16-row and shared-K/V kernels: their tiles differ
@@ -759,7 +761,7 @@ F32Plan f32_plan(int B, int H, int Nq, int Nk, int causal, int num_cus, bool hav
         const double c16 = rounds(t16) * 4.0 * ((n + 15) / 16);
         const double c32 = rounds(t32) * 3.6 * ((n + 7) / 8);
         const double c32s = rounds(2 * t32) * (3.6 * (((n + 1) / 2 + 7) / 8) + 3.0);
-        if (have_ws && c32s < c32 && c32s < c16) return F32Plan::Rows32Split;
+        if (have_ws && c32s < 0.97 * std::min(c16, c32)) return F32Plan::Rows32Split;
         return c32 < c16 ? F32Plan::Rows32 : F32Plan::Rows16;
     }
     if (FA2_F32_SHARED && groups >= num_cus) return F32Plan::Shared;

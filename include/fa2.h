@@ -131,8 +131,10 @@ fa2_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, flo
  * until the process ends.
  *   Errors   A shape whose workspace (attn_fwd_workspace_size) exceeds
  *            FA2_NOALLOC_SCRATCH_BYTES returns FA2_ERR_UNSUPPORTED (on a
- *            256-CU MI355X only a few head-dimension-128 shapes with few
- *            query tiles); use attn_fwd_ws for those.  FA2_ERR_DEVICE if the
+ *            256-CU MI355X: a few head-dimension-128 shapes with few query
+ *            tiles, and unmasked float32 head-dimension-64 shapes of 1986 or
+ *            more 32-row query tiles that would split their keys in two);
+ *            use attn_fwd_ws for those.  FA2_ERR_DEVICE if the
  *            array's device address cannot be obtained.
  *   Races    All attn_fwd_noalloc calls on one device share its array, which
  *            keeps the last call's contents: calls that can overlap in time on
