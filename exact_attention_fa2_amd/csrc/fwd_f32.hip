@@ -129,10 +129,11 @@ constexpr int part_floats() {
 // writes its partial state to `part`, then swaps `tag` (a 64-bit value drawn
 // for this launch) into the tile's handshake word; the one that gets `tag`
 // back is second, merges both states and writes O and LSE, and sets the word
-// to 0 again.  The partial state goes through device-scope stores and loads
-// (written through to, and read from, the point where all XCDs' caches
-// agree) so neither side needs a cache-wide write-back or invalidate; the
-// swap is issued only after those stores have completed.
+// to 0 again.  The partial state goes through system-scope stores and loads
+// (written through to memory and read from it, past every cache), and the
+// swap is a system-scope atomic issued only after those stores have
+// completed, so neither side needs a cache-wide write-back or invalidate
+// (a fence would do both to the whole L2 of the XCD).
 template <int D, bool CAUSAL, int RB, int NCH>
 __global__ __launch_bounds__((rows_waves<D, RB>() * 64), 1) void fwd_f32_rows_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
@@ -394,22 +395,25 @@ __global__ __launch_bounds__((rows_waves<D, RB>() * 64), 1) void fwd_f32_rows_ke
 #pragma unroll
         for (int w = 0; w < W; ++w) o += s_m[w][row] * *reinterpret_cast<const f32x4 *>(&s_o[w][row][d]);
 
-        // Publish this chunk's state (cache policy 16 = device scope), wait
-        // until every store of the workgroup has completed, then swap the tag.
-        constexpr int kDev = 16;
+        // Publish this chunk's state (cache policy 17 = SC0 | SC1, system
+        // scope), wait until every store of the workgroup has completed, then
+        // swap the tag.
+        constexpr int kSys = 17;
         constexpr int PF = part_floats<QT, D>();
         const auto rmine = make_rsrc(part + ((size_t)unit * NCH + chunk) * PF, PF * 4);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rmine, (row * D + d) * 4, 0, kDev);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rmine, (row * D + d) * 4, 0, kSys);
         if (d == 0) {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_mg[row]), rmine, (QT * D + row) * 4, 0, kDev);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_lg[row]), rmine, (QT * D + QT + row) * 4, 0, kDev);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_mg[row]), rmine, (QT * D + row) * 4, 0, kSys);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_lg[row]), rmine, (QT * D + QT + row) * 4, 0, kSys);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0) {
-            const unsigned long long old = atomicExch(&tags[unit], tag);
+            const unsigned long long old =
+                __hip_atomic_exchange(&tags[unit], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             const int second = old == tag;
-            if (second) atomicExch(&tags[unit], 0ull);  // ready for the next launch
+            if (second)  // ready for the next launch
+                __hip_atomic_exchange(&tags[unit], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             s_second = second;
         }
         __syncthreads();
@@ -418,9 +422,9 @@ __global__ __launch_bounds__((rows_waves<D, RB>() * 64), 1) void fwd_f32_rows_ke
         // Second: merge the two chunks' states in chunk order (the same
         // arithmetic whichever workgroup does it) and write O and LSE.
         const auto rother = make_rsrc(part + ((size_t)unit * NCH + (chunk ^ 1)) * PF, PF * 4);
-        const f32x4 oo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rother, (row * D + d) * 4, 0, kDev));
-        const float mo = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rother, (QT * D + row) * 4, 0, kDev));
-        const float lo = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rother, (QT * D + QT + row) * 4, 0, kDev));
+        const f32x4 oo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rother, (row * D + d) * 4, 0, kSys));
+        const float mo = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rother, (QT * D + row) * 4, 0, kSys));
+        const float lo = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rother, (QT * D + QT + row) * 4, 0, kSys));
         const float mm = s_mg[row], lm = s_lg[row];
         const bool c0 = chunk == 0;
         const float m0 = c0 ? mm : mo, m1 = c0 ? mo : mm;
