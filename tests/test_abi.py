@@ -150,9 +150,26 @@ def test_workspace_size_plan():
     assert fa2.workspace_size(1, 2, 1024, 1024, 96, 0, f16) == 0
     assert fa2.workspace_size(1, 2, 1024, 512, 64, 1, f16) == 0
     assert fa2.workspace_size(0, 2, 1024, 1024, 64, 0, f16) == 0
-    # float32: one head of 4096 rows is split, many heads are not
-    assert fa2.workspace_size(1, 1, 4096, 4096, 64, 0, f32) >= 0
+    # float32 at D = 64, unmasked, where 32-row tiles split in two cover the
+    # device: the key split with the in-kernel merge needs a 64-bit handshake
+    # word per 32-row tile (padded to 256 bytes) and two partial states of
+    # 32 x 64 + 2 x 32 floats per tile.  One head of 4096 rows: 128 tiles.
+    part = lambda tiles: (tiles * 8 + 255) // 256 * 256 + tiles * 2 * (32 * 64 + 64) * 4  # noqa: E731
+    assert fa2.workspace_size(1, 1, 4096, 4096, 64, 0, f32) == part(128)
+    assert fa2.workspace_size(1, 1, 4090, 4096, 64, 0, f32) == part(128)
+    assert fa2.workspace_size(1, 4, 1000, 4000, 64, 0, f32) == part(128)
+    # ... no split where it would save under 3% (short keys, or tile counts
+    # that fill whole rounds), causal shapes (the 16-row kernel), and many
+    # heads (32-row tiles without a split)
+    assert fa2.workspace_size(1, 1, 4096, 16, 64, 0, f32) == 0
+    assert fa2.workspace_size(1, 2, 4096, 4096, 64, 0, f32) == 0
+    assert fa2.workspace_size(3, 1, 3000, 2000, 64, 0, f32) == 0
+    assert fa2.workspace_size(1, 1, 4096, 4096, 64, 1, f32) == 0
     assert fa2.workspace_size(8, 48, 256, 256, 64, 0, f32) == 0
+    # fewer rows: the shared kernel's key split and the combine, D + 2 floats
+    # per row and chunk
+    need32 = fa2.workspace_size(1, 2, 1024, 1024, 64, 0, f32)
+    assert need32 > 0 and need32 % (2 * 1024 * 66 * 4) == 0
 
 
 def _bwd(q=1, k=1, v=1, o=1, g=1, lse=1, dq=1, dk=1, dv=1, delta=1, B=1, H=1, Nq=4, Nk=4, D=64,
