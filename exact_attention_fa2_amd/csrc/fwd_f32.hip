@@ -4,24 +4,32 @@
 //
 // Method ("Flash attention, f32": sections One block of queries per CTA, The
 // loop over keys, Online softmax, After the loop; "Flash Attention"
-// (aarnphm.xyz): Deriving the online softmax, tile form).  A workgroup owns 16
-// query rows, read from memory once into LDS and from there into every wave's
-// registers.  Its 16 waves (8 at D = 128) each walk a contiguous slice of the
-// keys, 16 keys a step, carrying a running max m, the running denominator l
-// and the unnormalised output O.  O and l are rescaled by exp(m_old - m_new)
-// only when a step's scores overtake m far enough that some exp(s - m) would
-// pass 2^8 (or the row has no m yet); below that, keeping the older m changes
-// only the common factor of O and l, which the final O/l cancels.  At the end
-// the waves' partial states are merged with the (m, l) monoid of "Flash
+// (aarnphm.xyz): Deriving the online softmax, tile form).  A workgroup owns
+// one or two blocks of 16 query rows, read from memory once into LDS and from
+// there into every wave's registers.  Its waves (16 with one block at D = 64,
+// else 8) each walk a contiguous slice of the workgroup's keys, 16 keys a
+// step, carrying a running max m, the running denominator l and the
+// unnormalised output O.  O and l are rescaled by exp(m_old - m_new) only when
+// a step's scores overtake m far enough that some exp(s - m) would pass 2^8
+// (or the row has no m yet); below that, keeping the older m changes only the
+// common factor of O and l, which the final O/l cancels.  At the end the
+// waves' partial states are merged with the (m, l) monoid of "Flash
 // Attention" (section Deriving the online softmax) through LDS, then O/l and
-// LSE = m + ln l are written.
+// LSE = m + ln l are written -- or, when a tile's keys were split between two
+// workgroups, the two states are merged the same way by the second of them
+// to finish.
 //
 // Why split the keys across waves: one head of 4096 rows gives only 256 tiles
-// of 16 rows, one per compute unit; splitting each tile's keys 16 ways puts
-// four waves on every SIMD, enough to keep the matrix cores fed while other
-// waves wait for their K/V loads.  The pages' FlashAttention-2 prefers
-// splitting queries across warps ("Flash Attention", section FlashAttention 2);
-// this kernel keeps that across workgroups and splits keys only inside one.
+// of 16 rows, or 128 of 32; splitting each tile's keys among the workgroup's
+// waves puts two to four waves on every SIMD, enough to keep the matrix cores
+// fed while other waves wait for their K/V loads, and with 32-row tiles the
+// keys are also split between two workgroups so that every compute unit has
+// one.  The pages' FlashAttention-2 prefers splitting queries across warps
+// ("Flash Attention", section FlashAttention 2); these kernels keep that
+// across workgroups where there are enough rows.
+//
+// A third kernel, for many query rows, shares each K/V block between four
+// 16-row tiles through LDS (namespace shared below).
 //
 // Lane layout (lane = 16*g + c):
 //   S^T = K Q^T per 16-key step: lane holds scores of query c for keys 4g..4g+3;
@@ -43,8 +51,8 @@ namespace fa2 {
 namespace {
 
 constexpr int kD = 64;
-constexpr int kQT = 16;     // query rows per workgroup
-constexpr int kWaves = 16;  // waves per workgroup (4 per SIMD), each on its own key slice
+constexpr int kQT = 16;     // query rows of a row block (one 16x16 MFMA tile)
+constexpr int kWaves = 16;  // waves of a shared-K/V workgroup (4 per SIMD)
 constexpr int kStep = 16;   // keys per step
 // A step's exponentials are kept, taken against the running max as it stands,
 // when each lane's four P values sum to at most this (every P <= 2^8, far from
