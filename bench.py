@@ -210,6 +210,11 @@ def fwd_extra_cfgs():
                                0.125, False, 0),
              workloads.Prefill("B4 H12 M=1024 N=4096 D64 f16", 4, 12, 1024, 4096, 64, "f16",
                                0.125, False, 0)]
+    # the headline's f32 kernel on more rows and longer keys
+    cfgs += [workloads.Prefill("B4 H12 M=N=2048 D64 f32", 4, 12, 2048, 2048, 64, "f32",
+                               0.125, False, 0),
+             workloads.Prefill("single-head f32 Nq=Nk=8192 D64", 1, 1, 8192, 8192, 64, "f32",
+                               0.125, False, 0)]
     return cfgs
 
 
