@@ -61,6 +61,16 @@ def test_two_calls_in_a_row_second_smaller(dt):
         one_pair(1, 2, 4096, 4096, 64, dt, True, 32)
 
 
+def test_f32_tile_split_on_the_scratch_array():
+    """The float32 split whose two workgroups per tile meet through handshake
+    words: on the scratch array those words first hold whatever an earlier
+    call left there (here the partials of a split-and-combine shape), and each
+    call must leave them ready for the next one."""
+    one_pair(1, 2, 1024, 1024, 64, "f32", False, 35)   # keys split, merged by the combine
+    one_pair(1, 1, 4096, 4096, 64, "f32", False, 36)   # 32-row tiles, keys in two chunks
+    one_pair(1, 1, 4096, 4096, 64, "f32", False, 37)
+
+
 def test_d128_split_and_no_split_shapes():
     import torch
     one_pair(1, 2, 4096, 4096, 128, "f16", False, 33)
