@@ -781,11 +781,14 @@ F32Plan f32_plan(int B, int H, int Nq, int Nk, int causal, int num_cus, bool hav
 }
 
 // Workspace of the 32-row kernel with its keys split in two: a 64-bit
-// handshake word per tile, then two partial states per tile.
-size_t rows32_split_bytes(long long tiles) {
-    const size_t words = ((size_t)tiles * 8 + 255) / 256 * 256;
-    return words + (size_t)tiles * 2 * part_floats<kRows32, kD>() * sizeof(float);
-}
+// handshake word per tile (the words padded to 256 bytes), then two partial
+// states per tile.
+struct Rows32SplitLayout {
+    size_t words, bytes;
+    explicit Rows32SplitLayout(long long tiles)
+        : words(((size_t)tiles * 8 + 255) / 256 * 256),
+          bytes(words + (size_t)tiles * 2 * part_floats<kRows32, kD>() * sizeof(float)) {}
+};
 
 // A fresh 64-bit value per launch for the handshake words: a counter with a
 // random start, stepped by the golden-ratio increment and scrambled by the
@@ -793,9 +796,15 @@ size_t rows32_split_bytes(long long tiles) {
 // number generators", 2014); forced odd, so never 0 (a word's resting value).
 unsigned long long next_tag() {
     static std::atomic<unsigned long long> state{[] {
-        std::random_device rd;
-        return ((unsigned long long)rd() << 32) ^ rd() ^
-               (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+        unsigned long long seed =
+            (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+        seed ^= (unsigned long long)(uintptr_t)&seed;
+        try {  // no exception may leave the C ABI; the clock alone is a usable start
+            std::random_device rd;
+            seed ^= ((unsigned long long)rd() << 32) ^ rd();
+        } catch (...) {
+        }
+        return seed;
     }()};
     unsigned long long z = state.fetch_add(0x9E3779B97F4A7C15ull) + 0x9E3779B97F4A7C15ull;
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -809,7 +818,7 @@ size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, int 
     if (D != kD) return 0;  // D = 128 always runs the 16-row kernel
     switch (f32_plan(B, H, Nq, Nk, causal, num_cus, true)) {
         case F32Plan::Rows32Split:
-            return rows32_split_bytes((long long)B * H * ((Nq + kRows32 - 1) / kRows32));
+            return Rows32SplitLayout((long long)B * H * ((Nq + kRows32 - 1) / kRows32)).bytes;
         case F32Plan::SharedSplit: {
             const int c = f32_chunks(B, H, Nq, Nk, num_cus);
             return (size_t)B * H * Nq * c * (kD + 2) * sizeof(float);
@@ -864,9 +873,9 @@ fa2_status launch_fwd_f32(const FwdArgs &a, hipStream_t st) {
     if (plan == F32Plan::Rows32Split) {
         // each 32-row tile's keys in two chunks, merged by the second of its
         // two workgroups
-        const long long tiles = (long long)a.B * a.H * ((a.Nq + kRows32 - 1) / kRows32);
+        const Rows32SplitLayout lay((long long)a.B * a.H * ((a.Nq + kRows32 - 1) / kRows32));
         auto *tags = (unsigned long long *)a.ws;
-        float *part = (float *)((char *)a.ws + (need - (size_t)tiles * 2 * part_floats<kRows32, kD>() * sizeof(float)));
+        float *part = (float *)((char *)a.ws + lay.words);
         return launch_rows<kD, 2, 2>(a, sl2, st, part, tags, next_tag());
     }
     if (plan == F32Plan::SharedSplit && ws_ok) {
