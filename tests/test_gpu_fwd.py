@@ -243,21 +243,42 @@ def test_running_max_moves_often(order, dt, shape):
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.125, 2.0])
-def test_f32_shared_kernel_unusual_scales(scale):
-    """The float32 shared-K/V kernel (256 groups of 64 rows: one per compute
-    unit) with scale 0, a negative scale and a large one, causal and not."""
+def test_f32_unusual_scales(scale):
+    """Scale 0, a negative scale and a large one on the float32 kernels:
+    B4 H16 N256 runs 32-row tiles unmasked and the shared-K/V kernel (256
+    groups of 64 rows, one per compute unit) causal; one head of 4096 rows
+    runs 32-row tiles with the keys split in two and merged in the kernel."""
     import torch
-    q, k, v = seeded(4, 16, 256, 256, 64, "f32", 15)
+    for (B, H, N), causals in (((4, 16, 256), (False, True)), ((1, 1, 4096), (False,))):
+        q, k, v = seeded(B, H, N, N, 64, "f32", 15)
+        q64, k64, v64 = (inputs.to_f64(x, "f32") for x in (q, k, v))
+        tq, tk, tv = upload(q, "f32"), upload(k, "f32"), upload(v, "f32")
+        for causal in causals:
+            o, lse = fa2.attn_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=True)
+            torch.cuda.synchronize()
+            ro, rl = oracle.attn(q64, k64, v64, scale, causal)
+            tag = "f32 B%d H%d N%d scale %g causal=%d" % (B, H, N, scale, causal)
+            assert_close(tag + " O", download_f64(o), ro, TOL["f32"])
+            assert_close(tag + " LSE", download_f64(lse), rl, LSE_TOL)
+
+
+def test_f32_split_tile_large_score_shift():
+    """The float32 key split merged in the kernel with scores near 100 (far
+    past exp's overflow): K' = K + u shifts every score of a row by the same
+    amount, so both chunks of a tile carry large maxima."""
+    import torch
+    q, k, v = seeded(1, 1, 4096, 4096, 64, "f32", 10)
+    k = k.copy()
+    k[..., :4] += 64.0
+    assert fa2.workspace_size(1, 1, 4096, 4096, 64, False, fa2.FA2_F32) > 0
     q64, k64, v64 = (inputs.to_f64(x, "f32") for x in (q, k, v))
     tq, tk, tv = upload(q, "f32"), upload(k, "f32"), upload(v, "f32")
-    for causal in (False, True):
-        o, lse = fa2.attn_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=True)
-        torch.cuda.synchronize()
-        ro, rl = oracle.attn(q64, k64, v64, scale, causal)
-        assert_close("f32 shared scale %g causal=%d O" % (scale, causal), download_f64(o), ro,
-                     TOL["f32"])
-        assert_close("f32 shared scale %g causal=%d LSE" % (scale, causal), download_f64(lse), rl,
-                     LSE_TOL)
+    o, lse = fa2.attn_fwd(tq, tk, tv, scale=0.5, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn(q64, k64, v64, 0.5, False)
+    assert np.max(np.abs(rl)) > 100
+    assert_close("f32 split shift O", download_f64(o), ro, TOL["f32"])
+    assert_close("f32 split shift LSE", download_f64(lse), rl, LSE_TOL)
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
@@ -348,6 +369,9 @@ def test_f32_rows32(shape):
             first = (o.clone(), lse.clone())
         elif seed == 16:
             assert torch.equal(o, first[0]) and torch.equal(lse, first[1]), "not deterministic"
+    o = fa2.attn_fwd(tq, tk, tv, scale=0.125, workspace=ws)  # no LSE asked for
+    torch.cuda.synchronize()
+    assert_close("rows32 without LSE O", download_f64(o), ro, TOL["f32"])
     o, lse = fa2.attn_fwd(tq, tk, tv, scale=0.125, return_lse=True, use_workspace=False)
     torch.cuda.synchronize()
     assert_close("rows32 shape without workspace O", download_f64(o), ro, TOL["f32"])
