@@ -3,10 +3,13 @@
 // frees or synchronises; every launch goes on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <random>
 
 #include "fa2_internal.h"
 
@@ -64,6 +67,32 @@ int esize(fa2_dtype dt) { return dt == FA2_F32 ? 4 : 2; }
 bool valid_dtype(int dt) { return dt == FA2_F32 || dt == FA2_F16 || dt == FA2_BF16; }
 
 }  // namespace
+
+namespace fa2 {
+
+// A counter with a random start, stepped by the golden-ratio increment and
+// scrambled by the SplitMix64 finaliser (Steele, Lea and Flood, "Fast
+// splittable pseudorandom number generators", 2014); forced odd, so never 0
+// (a handshake word's resting value).
+unsigned long long next_launch_tag() {
+    static std::atomic<unsigned long long> state{[] {
+        unsigned long long seed =
+            (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+        seed ^= (unsigned long long)(uintptr_t)&seed;
+        try {  // no exception may leave the C ABI; the clock alone is a usable start
+            std::random_device rd;
+            seed ^= ((unsigned long long)rd() << 32) ^ rd();
+        } catch (...) {
+        }
+        return seed;
+    }()};
+    unsigned long long z = state.fetch_add(0x9E3779B97F4A7C15ull) + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return (z ^ (z >> 31)) | 1ull;
+}
+
+}  // namespace fa2
 
 namespace {
 

@@ -48,6 +48,10 @@ struct FwdArgs {
     size_t ws_bytes;  // its size
 };
 
+// A fresh odd 64-bit value per call (never 0), for the per-launch tags of the
+// in-kernel key-chunk merges; thread-safe.
+unsigned long long next_launch_tag();
+
 // float32 forward on float32 matrix cores, D = 64 or 128.
 fa2_status launch_fwd_f32(const FwdArgs &a, hipStream_t st);
 size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, int num_cus);

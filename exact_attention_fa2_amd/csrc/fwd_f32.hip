@@ -39,9 +39,6 @@
 // The contraction index of both products is only a pairing of operand slots,
 // so A and B just have to agree on it.
 #include <algorithm>
-#include <atomic>
-#include <chrono>
-#include <random>
 
 #include "fa2_device.h"
 #include "fa2_internal.h"
@@ -790,28 +787,6 @@ struct Rows32SplitLayout {
           bytes(words + (size_t)tiles * 2 * part_floats<kRows32, kD>() * sizeof(float)) {}
 };
 
-// A fresh 64-bit value per launch for the handshake words: a counter with a
-// random start, stepped by the golden-ratio increment and scrambled by the
-// SplitMix64 finaliser (Steele, Lea and Flood, "Fast splittable pseudorandom
-// number generators", 2014); forced odd, so never 0 (a word's resting value).
-unsigned long long next_tag() {
-    static std::atomic<unsigned long long> state{[] {
-        unsigned long long seed =
-            (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
-        seed ^= (unsigned long long)(uintptr_t)&seed;
-        try {  // no exception may leave the C ABI; the clock alone is a usable start
-            std::random_device rd;
-            seed ^= ((unsigned long long)rd() << 32) ^ rd();
-        } catch (...) {
-        }
-        return seed;
-    }()};
-    unsigned long long z = state.fetch_add(0x9E3779B97F4A7C15ull) + 0x9E3779B97F4A7C15ull;
-    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-    return (z ^ (z >> 31)) | 1ull;
-}
-
 }  // namespace
 
 size_t f32_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, int num_cus) {
@@ -876,7 +851,7 @@ fa2_status launch_fwd_f32(const FwdArgs &a, hipStream_t st) {
         const Rows32SplitLayout lay((long long)a.B * a.H * ((a.Nq + kRows32 - 1) / kRows32));
         auto *tags = (unsigned long long *)a.ws;
         float *part = (float *)((char *)a.ws + lay.words);
-        return launch_rows<kD, 2, 2>(a, sl2, st, part, tags, next_tag());
+        return launch_rows<kD, 2, 2>(a, sl2, st, part, tags, next_launch_tag());
     }
     if (plan == F32Plan::SharedSplit && ws_ok) {
         // few rows: split the keys into c chunks, then merge the partials

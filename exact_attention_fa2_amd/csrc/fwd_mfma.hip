@@ -9,7 +9,8 @@
 // 256 rows with two slabs per wave (QG = 2, half the LDS reads per flop) when
 // the tiles fill the device in whole rounds, and walks the keys in blocks of
 // 64 staged through LDS; with few tiles the keys are also cut into chunks
-// whose partial states the combine kernel merges.  Per block and wave:
+// whose partial states the combine kernel merges, or, with two chunks, the
+// second workgroup of the pair to finish.  Per block and wave:
 //     S^T = K Q^T                    (D/8 MFMAs, f32 accumulate)
 //     m_new = max(m, rowmax S);  P = exp(S - m);  l = l*corr + rowsum P
 //     O^T = corr*O^T + V^T P^T       (D/8 MFMAs, P rounded to the input dtype)
@@ -168,7 +169,11 @@ struct MfmaT<2> {
 // partials); the workgroup writes, per row and chunk, O_s (not divided),
 // m_s (natural-log units), the denominator of the rounded P (lt, which
 // normalises O) and, with WLSE, that of the f32 P (l, for the LSE), and the
-// combine kernel merges them.
+// combine kernel merges them.  With tags (gridDim.y = 2) the two workgroups
+// of a tile merge their states themselves: each publishes its state with
+// system-scope stores and swaps the launch's tag into tags[blockIdx.x]; the
+// one that finds the tag already there merges both in chunk order and writes
+// O and LSE (no combine launch).
 // D: head dimension, 64 or 128 (128 only with QG = 1: its Q operand and O
 // accumulator take twice the registers, and its K/V buffers 64 KB of LDS).
 template <int D, int DT, bool CAUSAL, bool WLSE, bool SPLIT, int QG>
@@ -176,8 +181,8 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
     float *__restrict__ o_part, float *__restrict__ m_part, float *__restrict__ l_part,
-    float *__restrict__ l2_part, int Nq, int Nk, float scale_log2, int n_qtiles, int n_tiles,
-    int snake) {
+    float *__restrict__ l2_part, unsigned long long *__restrict__ tags, unsigned long long tag,
+    int Nq, int Nk, float scale_log2, int n_qtiles, int n_tiles, int snake) {
     static_assert((D == 64 || D == 128) && (D == 64 || QG == 1), "head dimension");
     constexpr int kD = D;
     constexpr int NC = D / 16;                      // 16-wide contraction chunks of S^T = K Q^T
@@ -552,10 +557,9 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         float *stage = reinterpret_cast<float *>(wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1);
-        const size_t nch = gridDim.y;
-#pragma unroll
-        for (int g = 0; g < QG; ++g) {
-            const int myq = qw + 32 * g + ql;
+        // Group g's unnormalised O into the wave's stage: row ql, columns
+        // swizzled by 4 (ql % 8) so that the rows' f32x4 reads do not conflict.
+        auto stage_o = [&](int g) __attribute__((always_inline)) {
 #pragma unroll
             for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
@@ -564,6 +568,108 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
                     *reinterpret_cast<f32x4 *>(stage + ql * kD + ((32 * dt + 8 * g4 + 4 * h) ^ (4 * (ql & 7)))) =
                         f32x4{oacc[g][dt][r], oacc[g][dt][r + 1], oacc[g][dt][r + 2], oacc[g][dt][r + 3]};
                 }
+        };
+        if (tags) {
+            // The pair's states, per (tile, chunk) one block of PF floats:
+            // O [ROWS][D], then m (base 2), lt and l per row.  Stores and
+            // loads use cache policy 17 (SC0 | SC1, system scope), so the
+            // partner reads them from memory whichever XCD it runs on; the
+            // tag swap follows this workgroup's last completed store.
+            constexpr int kSys = 17;
+            constexpr int PF = ROWS * (kD + 3);
+            const int chunk = blockIdx.y;
+            const auto rmine = make_rsrc(o_part + ((size_t)blockIdx.x * 2 + chunk) * PF, PF * 4);
+            const auto rother = make_rsrc(o_part + ((size_t)blockIdx.x * 2 + (chunk ^ 1)) * PF, PF * 4);
+#pragma unroll
+            for (int g = 0; g < QG; ++g) {
+                const int rl = wave * 32 * QG + 32 * g;  // group g's first row within the tile
+                stage_o(g);
+                if (h == 0) {
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m[g]), rmine, (ROWS * kD + rl + ql) * 4, 0, kSys);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lt[g]), rmine,
+                                                          (ROWS * kD + ROWS + rl + ql) * 4, 0, kSys);
+                    if constexpr (WLSE)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l[g]), rmine,
+                                                              (ROWS * kD + 2 * ROWS + rl + ql) * 4, 0, kSys);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int hc = 0; hc < D / 64; ++hc) {
+                        const int row = 4 * j + (lane >> 4);
+                        const int col = 64 * hc + 4 * (lane & 15);
+                        const f32x4 val =
+                            *reinterpret_cast<const f32x4 *>(stage + row * kD + (col ^ (4 * (row & 7))));
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), rmine,
+                                                               ((rl + row) * kD + col) * 4, 0, kSys);
+                    }
+            }
+            __shared__ int s_second;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0) {
+                const unsigned long long old =
+                    __hip_atomic_exchange(&tags[blockIdx.x], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                const int second = old == tag;
+                if (second)  // ready for the next launch
+                    __hip_atomic_exchange(&tags[blockIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                s_second = second;
+            }
+            __syncthreads();
+            if (!s_second) return;
+
+            // Second: per row the weights of the two states (lane ql, either
+            // half, holds row ql's), then O in chunk order -- the same
+            // arithmetic whichever workgroup of the pair does it.
+            const bool c0 = chunk == 0;
+#pragma unroll
+            for (int g = 0; g < QG; ++g) {
+                const int rl = wave * 32 * QG + 32 * g;
+                const float mo = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rother, (ROWS * kD + rl + ql) * 4, 0, kSys));
+                const float lto = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(rother, (ROWS * kD + ROWS + rl + ql) * 4, 0, kSys));
+                const float m0 = c0 ? m[g] : mo, m1 = c0 ? mo : m[g];
+                const float lt0 = c0 ? lt[g] : lto, lt1 = c0 ? lto : lt[g];
+                const float mg = fmax_nan(m0, m1);
+                const float w0 = m0 == -INFINITY ? 0.f : exp2f_fast(m0 - mg);
+                const float w1 = m1 == -INFINITY ? 0.f : exp2f_fast(m1 - mg);
+                const float inv = 1.f / (w0 * lt0 + w1 * lt1);
+                const float a0 = w0 * inv, a1 = w1 * inv;
+                if constexpr (WLSE) {
+                    const float lo = __uint_as_float(
+                        __builtin_amdgcn_raw_buffer_load_b32(rother, (ROWS * kD + 2 * ROWS + rl + ql) * 4, 0, kSys));
+                    const float l0 = c0 ? l[g] : lo, l1 = c0 ? lo : l[g];
+                    const int myq = q0 + rl + ql;
+                    if (h == 0 && myq < Nq) LSE[(size_t)bh * Nq + myq] = (mg + log2f_fast(w0 * l0 + w1 * l1)) * kLn2;
+                }
+                if (QG > 1) stage_o(g);  // (with one group the stage still holds it)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int row = 4 * j + (lane >> 4);
+                    const float a0r = __shfl(a0, row), a1r = __shfl(a1, row);
+                    const int q = q0 + rl + row;
+#pragma unroll
+                    for (int hc = 0; hc < D / 64; ++hc) {
+                        const int col = 64 * hc + 4 * (lane & 15);
+                        const f32x4 own =
+                            *reinterpret_cast<const f32x4 *>(stage + row * kD + (col ^ (4 * (row & 7))));
+                        const f32x4 oth = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rother, ((rl + row) * kD + col) * 4, 0, kSys));
+                        const f32x4 o0 = c0 ? own : oth, o1 = c0 ? oth : own;
+                        const f32x4 o = a0r * o0 + a1r * o1;
+                        if (q < Nq)
+                            *reinterpret_cast<u32x2 *>(O + ((size_t)bh * Nq + q) * kD + col) =
+                                u32x2{pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3])};
+                    }
+                }
+            }
+            return;
+        }
+        const size_t nch = gridDim.y;
+#pragma unroll
+        for (int g = 0; g < QG; ++g) {
+            const int myq = qw + 32 * g + ql;
+            stage_o(g);
             if (myq < Nq && h == 0) {
                 const size_t pidx = ((size_t)bh * Nq + myq) * nch + blockIdx.y;
                 m_part[pidx] = m[g] == -INFINITY ? -INFINITY : m[g] * kLn2;  // natural-log units
@@ -978,6 +1084,16 @@ size_t part_bytes(const FwdArgs &a, int chunks) {
     return (size_t)a.B * a.H * a.Nq * chunks * (a.D + 3) * sizeof(float);
 }
 
+// Workspace of a two-chunk split merged in the kernel: one 8-byte handshake
+// word per tile (the area padded to 256 bytes), then per tile and chunk a
+// state block of rows * (D + 3) floats.
+struct PairLayout {
+    size_t tag_bytes, bytes;
+    PairLayout(long long tiles, int rows, int D)
+        : tag_bytes(((size_t)tiles * 8 + 255) & ~(size_t)255),
+          bytes(tag_bytes + (size_t)tiles * 2 * rows * (D + 3) * sizeof(float)) {}
+};
+
 // CUs per XCD for the causal snake order (0: keep longest first): only when
 // all tiles fit one round of workgroup slots and every XCD holds whole heads.
 template <int D, int QG>
@@ -993,7 +1109,15 @@ template <int D, int DT, bool CAUSAL, bool WLSE, int QG>
 fa2_status launch_q(const FwdArgs &a, const Plan &p, hipStream_t st) {
     const uint16_t *q = (const uint16_t *)a.q, *k = (const uint16_t *)a.k, *v = (const uint16_t *)a.v;
     const float sl2 = a.scale * kLog2e;
-    if (p.chunks > 1 && a.ws && a.ws_bytes >= part_bytes(a, p.chunks)) {
+    const PairLayout pair(p.n_tiles, kWaves * 32 * QG, D);
+    if (p.chunks == 2 && a.ws && a.ws_bytes >= pair.bytes) {
+        return launch(fwd_mfma_kernel<D, DT, CAUSAL, WLSE, true, QG>, dim3((unsigned)p.n_tiles, 2u),
+                      dim3(kWaves * 64), st, q, k, v, (uint16_t *)a.o, a.lse,
+                      (float *)((char *)a.ws + pair.tag_bytes), (float *)nullptr, (float *)nullptr,
+                      (float *)nullptr, (unsigned long long *)a.ws, next_launch_tag(), a.Nq, a.Nk, sl2,
+                      p.n_qtiles, p.n_tiles, 0);
+    }
+    if (p.chunks > 2 && a.ws && a.ws_bytes >= part_bytes(a, p.chunks)) {
         const size_t n = (size_t)a.B * a.H * a.Nq * p.chunks;
         float *o_part = (float *)a.ws;
         float *m_part = o_part + n * D;
@@ -1001,8 +1125,9 @@ fa2_status launch_q(const FwdArgs &a, const Plan &p, hipStream_t st) {
         float *l2_part = l_part + n;
         fa2_status s = launch(fwd_mfma_kernel<D, DT, CAUSAL, WLSE, true, QG>,
                               dim3((unsigned)p.n_tiles, (unsigned)p.chunks), dim3(kWaves * 64), st,
-                              q, k, v, (uint16_t *)a.o, a.lse, o_part, m_part, l_part, l2_part, a.Nq,
-                              a.Nk, sl2, p.n_qtiles, p.n_tiles, 0);
+                              q, k, v, (uint16_t *)a.o, a.lse, o_part, m_part, l_part, l2_part,
+                              (unsigned long long *)nullptr, 0ull, a.Nq, a.Nk, sl2, p.n_qtiles,
+                              p.n_tiles, 0);
         if (s != FA2_OK) return s;
         return launch_combine_rows(o_part, m_part, l_part, a.o, a.lse, (size_t)a.B * a.H * a.Nq, D,
                                    p.chunks, DT == 1 ? FA2_F16 : FA2_BF16, st,
@@ -1010,8 +1135,8 @@ fa2_status launch_q(const FwdArgs &a, const Plan &p, hipStream_t st) {
     }
     return launch(fwd_mfma_kernel<D, DT, CAUSAL, WLSE, false, QG>, dim3((unsigned)p.n_tiles),
                   dim3(kWaves * 64), st, q, k, v, (uint16_t *)a.o, a.lse, (float *)nullptr,
-                  (float *)nullptr, (float *)nullptr, (float *)nullptr, a.Nq, a.Nk, sl2,
-                  p.n_qtiles, p.n_tiles, snake_cus<D, QG>(a, p));
+                  (float *)nullptr, (float *)nullptr, (float *)nullptr, (unsigned long long *)nullptr,
+                  0ull, a.Nq, a.Nk, sl2, p.n_qtiles, p.n_tiles, snake_cus<D, QG>(a, p));
 }
 
 template <int D, int DT, bool CAUSAL, bool WLSE>
@@ -1055,6 +1180,7 @@ size_t mfma_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, int
     (void)causal;
     const Plan p = plan(B, H, Nq, Nk, D, num_cus);
     if (p.rows || p.chunks <= 1) return 0;
+    if (p.chunks == 2) return PairLayout(p.n_tiles, kWaves * 32 * p.qg, D).bytes;
     return (size_t)B * H * Nq * p.chunks * (D + 3) * sizeof(float);
 }
 

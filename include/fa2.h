@@ -102,11 +102,14 @@ fa2_status attn_fwd(const void *q, const void *k, const void *v, void *o, float 
  * smaller workspace it runs exactly as attn_fwd.  The two paths may differ in
  * the last bits (the sums are grouped differently), each within the bounds
  * stated for attn_fwd.
- *   For unmasked float32 D = 64 shapes with few 32-row query tiles, the split
- *   is instead two key chunks per tile, whose workgroups meet at the end with
- *   no wait: each publishes its partial state, then swaps a 64-bit value drawn
- *   for this call into the tile's handshake word in the workspace; the one
- *   that gets the value back merges and writes o and lse, and resets the word.
+ *   Where the keys of each tile are split in exactly two chunks (f16 and
+ *   bf16, causal or not; and the float32 split of unmasked D = 64 shapes
+ *   with few 32-row query tiles), there is no combine launch: the tile's two
+ *   workgroups meet at the end with no wait.  Each publishes its partial
+ *   state, then swaps a 64-bit value drawn for this call into the tile's
+ *   handshake word in the workspace; the one that gets the value back merges
+ *   the two states in chunk order (so the result does not depend on which
+ *   one finished last), writes o and lse, and resets the word.
  *   workspace  device memory, 16-byte aligned, owned by the caller.  Its
  *              contents on entry do not matter: the handshake words are read
  *              before they are written, but only a word that already holds
@@ -131,10 +134,10 @@ fa2_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, flo
  * until the process ends.
  *   Errors   A shape whose workspace (attn_fwd_workspace_size) exceeds
  *            FA2_NOALLOC_SCRATCH_BYTES returns FA2_ERR_UNSUPPORTED (on a
- *            256-CU MI355X: a few head-dimension-128 shapes with few query
- *            tiles, and unmasked float32 head-dimension-64 shapes of 1986 or
- *            more 32-row query tiles that would split their keys in two);
- *            use attn_fwd_ws for those.  FA2_ERR_DEVICE if the
+ *            256-CU MI355X: head-dimension-128 shapes whose key split fills
+ *            every workgroup slot, and unmasked float32 head-dimension-64
+ *            shapes of 1986 or more 32-row query tiles that would split their
+ *            keys in two); use attn_fwd_ws for those.  FA2_ERR_DEVICE if the
  *            array's device address cannot be obtained.
  *   Races    All attn_fwd_noalloc calls on one device share its array, which
  *            keeps the last call's contents: calls that can overlap in time on

@@ -141,6 +141,19 @@ def test_workspace_size_plan():
     assert fa2.workspace_size(1, 4, 4096, 4096, 64, 0, bf16) == need
     # enough query tiles to fill the device: no split
     assert fa2.workspace_size(4, 12, 2048, 2048, 64, 0, f16) == 0
+    # a split in exactly two chunks is merged in the kernel: a 64-bit
+    # handshake word per 128-row tile (padded to 256 bytes), then per tile
+    # two states of 128 x (D + 3) floats.  B4 H12 with 1024 queries (384
+    # tiles, half the 768 slots) over 4096 keys; 64 tiles over 2500 keys (40
+    # blocks: two chunks of at least 16); D = 128 with 16 tiles over 300 keys
+    # (five blocks: two chunks of at least two)
+    pair = lambda tiles, d: (tiles * 8 + 255) // 256 * 256 + tiles * 2 * 128 * (d + 3) * 4  # noqa: E731
+    assert fa2.workspace_size(4, 12, 1024, 4096, 64, 0, f16) == pair(384, 64)
+    assert fa2.workspace_size(4, 12, 1024, 4096, 64, 0, bf16) == pair(384, 64)
+    assert fa2.workspace_size(1, 8, 1024, 2500, 64, 0, f16) == pair(64, 64)
+    assert fa2.workspace_size(1, 8, 2500, 2500, 64, 1, f16) == pair(160, 64)
+    assert fa2.workspace_size(1, 2, 1000, 300, 128, 0, bf16) == pair(16, 128)
+    assert fa2.workspace_size(1, 2, 300, 300, 128, 1, f16) == pair(6, 128)
     # D = 128 splits the same way, with D + 3 floats per row and chunk
     need128 = fa2.workspace_size(1, 2, 4096, 4096, 128, 1, f16)
     assert need128 > 0 and need128 % (2 * 4096 * 131 * 4) == 0

@@ -441,6 +441,67 @@ def test_long_keys_split_at_half_the_slots(dt):
         assert_close("half-slot split %s LSE" % tag, download_f64(lse)[:, heads], rl, LSE_TOL)
 
 
+# f16/bf16 shapes whose keys are split in exactly two chunks, the pair's
+# states merged in the kernel: (B, H, Nq, Nk, D, causal, flat heads checked
+# against the oracle, None for all)
+PAIR_SHAPES = [(1, 8, 1024, 2500, 64, False, None),  # 64 tiles over 40 key blocks, ragged keys
+               (1, 8, 2500, 2500, 64, True, None),   # causal: the early tiles' second chunk
+                                                     # holds no visible key for most rows
+               (1, 2, 1000, 300, 128, False, None),  # few tiles at D = 128, five key blocks
+               (1, 2, 300, 300, 128, True, None),
+               (4, 12, 1024, 4096, 64, False, [0, 23, 47])]  # B4 H12 1024 x 4096: three heads
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", PAIR_SHAPES, ids=lambda s: "x".join(map(str, s[:6])))
+def test_mfma_two_chunk_pair_merge(shape, dt):
+    """The two workgroups of a tile meet through a handshake word; the second
+    to finish merges both states.  The workspace starts out as random bytes
+    (the words' earlier contents must not matter), every call must leave the
+    words at 0, the same call twice must give the same bits (the merge runs
+    in chunk order whichever workgroup does it), a call on other values with
+    the same workspace must match the oracle again, and the call without LSE
+    must give the same O.  Without a workspace the shape runs unsplit."""
+    import torch
+    B, H, Nq, Nk, D, causal, heads = shape
+    code = fa2.FA2_F16 if dt == "f16" else fa2.FA2_BF16
+    tiles = B * H * ((Nq + 127) // 128)
+    need = fa2.workspace_size(B, H, Nq, Nk, D, causal, code)
+    assert need == (tiles * 8 + 255) // 256 * 256 + tiles * 2 * 128 * (D + 3) * 4, \
+        "the shape takes another schedule (need=%d)" % need
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
+    scale = 1 / np.sqrt(D)
+    pick = (lambda x: x) if heads is None else \
+        (lambda x: x.reshape((B * H, 1) + x.shape[2:])[heads])
+    first = None
+    for seed in (41, 41, 42):
+        q, k, v = seeded(B, H, Nq, Nk, D, dt, seed)
+        q64, k64, v64 = (pick(inputs.to_f64(x, dt)) for x in (q, k, v))
+        ro, rl = oracle.attn(q64, k64, v64, scale, causal)
+        wabs = oracle.attn(q64, k64, np.abs(v64), scale, causal)[0]
+        tq, tk, tv = upload(q, dt), upload(k, dt), upload(v, dt)
+        o, lse = fa2.attn_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=True, workspace=ws)
+        torch.cuda.synchronize()
+        tag = "pair %s seed %d" % (dt, seed)
+        got = pick(download_f64(o))
+        assert_close(tag + " O", got, ro, edge_tol(dt, ro, got, wabs))
+        assert_close(tag + " LSE", pick(download_f64(lse)), rl, LSE_TOL)
+        assert not ws[:8 * tiles].cpu().numpy().any(), "handshake words left set after the call"
+        if first is None:
+            first = (o.clone(), lse.clone())
+        elif seed == 41:
+            assert torch.equal(o, first[0]) and torch.equal(lse, first[1]), "not deterministic"
+    o_only = fa2.attn_fwd(tq, tk, tv, scale=scale, causal=causal, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o_only, o), "O differs between the runs with and without LSE"
+    o, lse = fa2.attn_fwd(tq, tk, tv, scale=scale, causal=causal, return_lse=True,
+                          use_workspace=False)
+    torch.cuda.synchronize()
+    got = pick(download_f64(o))
+    assert_close("pair shape without workspace O", got, ro, edge_tol(dt, ro, got, wabs))
+    assert_close("pair shape without workspace LSE", pick(download_f64(lse)), rl, LSE_TOL)
+
+
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", [(1, 2, 1024, 1024, True), (1, 1, 700, 700, False),
                                    (1, 3, 129, 2000, True), (2, 1, 300, 300, True)],

@@ -71,6 +71,15 @@ def test_f32_tile_split_on_the_scratch_array():
     one_pair(1, 1, 4096, 4096, 64, "f32", False, 37)
 
 
+def test_f16_pair_merge_on_the_scratch_array():
+    """The f16/bf16 split in two chunks, whose workgroups meet through
+    handshake words: first a split-and-combine shape leaves its partials in
+    the scratch array, then two pair shapes, the second smaller."""
+    one_pair(1, 4, 4096, 4096, 64, "f16", False, 38)   # four chunks, the combine kernel
+    one_pair(1, 8, 1024, 2500, 64, "f16", False, 39)   # two chunks, merged in the kernel
+    one_pair(1, 2, 300, 300, 128, "bf16", True, 40)
+
+
 def test_d128_split_and_no_split_shapes():
     import torch
     one_pair(1, 2, 4096, 4096, 128, "f16", False, 33)
