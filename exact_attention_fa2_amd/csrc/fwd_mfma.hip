@@ -1032,6 +1032,9 @@ struct Plan {
 #define FA2_MFMA_SPLIT_LONG 32  // also split when the tiles fill at most a quarter of the slots
                                 // and the keys span at least this many 64-key blocks (0: never)
 #endif
+#ifndef FA2_MFMA_PAIR
+#define FA2_MFMA_PAIR 1  // more shapes split in two, merged in the kernel (0: off)
+#endif
 #ifndef FA2_MFMA_SPLIT_LONG_HALF
 #define FA2_MFMA_SPLIT_LONG_HALF 64  // ... or at most half of the slots and at least this many
                                       // blocks (0: never)
@@ -1041,8 +1044,8 @@ struct Plan {
 // rounds of two per compute unit.  Keys: split the keys of each query tile
 // when the query tiles fill at most an eighth of the compute units (with
 // more, writing and merging the partials costs more than the idle units),
-// into at most one chunk per two key blocks.
-Plan plan(int B, int H, int Nq, int Nk, int D, int num_cus) {
+// into at most one chunk per two key blocks; with more tiles, see below.
+Plan plan(int B, int H, int Nq, int Nk, int D, int causal, int num_cus) {
     Plan p;
     p.qg = 1;
     if (FA2_MFMA_QG2 && D == 64) {
@@ -1076,6 +1079,25 @@ Plan plan(int B, int H, int Nq, int Nk, int D, int num_cus) {
             const long long c = std::min<long long>(slots / nt, nblk / 16);
             p.chunks = (int)std::max<long long>(1, std::min<long long>(c, 32));
         }
+    }
+    if (FA2_MFMA_PAIR && p.chunks == 1 && !p.rows && nt > 0) {
+        // Two chunks, merged in the kernel by the tile's second workgroup
+        // (no combine launch, so the split pays at shorter keys): when the
+        // tiles fill at most an eighth of the workgroup slots (keys of 16
+        // blocks or more), and at D = 64 when they fill at most half of the
+        // slots with keys of 32 blocks or more, if the tiles are causal (the
+        // halves of the longest tiles set the time) or if the halves lower
+        // the most tiles any compute unit holds (384 tiles: two on some CUs
+        // unsplit, three halves on every CU split; 256 tiles: one either way).
+        // Measured: B1 H8 1024^2 f16 14.4 -> 13.5 us, causal 17.7 -> 14.7,
+        // D = 128 21.5 -> 17.7; B2 H12 2048^2 causal 34.5 -> 29.9, unmasked
+        // 40.2 -> 39.3; B4 H12 1024 x 3000 56.9 -> 52.4; against B2 H8 2048^2
+        // unmasked 27.2 -> 29.1 and B1 H12 2048^2 D128 38.1 -> 39.8 split.
+        const long long slots = (long long)num_cus * (p.qg == 1 && D == 64 ? 3 : 2);
+        const bool fewer = (2 * nt + num_cus - 1) / num_cus < 2 * ((nt + num_cus - 1) / num_cus);
+        if ((8 * nt <= slots && nblk >= 16) ||
+            (D == 64 && 2 * nt <= slots && nblk >= 32 && (causal || fewer)))
+            p.chunks = 2;
     }
     return p;
 }
@@ -1162,7 +1184,7 @@ fa2_status launch_v(const FwdArgs &a, const Plan &p, hipStream_t st) {
 
 template <int D, int DT>
 fa2_status launch_dt(const FwdArgs &a, hipStream_t st) {
-    const Plan p = plan(a.B, a.H, a.Nq, a.Nk, D, a.num_cus);
+    const Plan p = plan(a.B, a.H, a.Nq, a.Nk, D, a.causal, a.num_cus);
     if (p.n_tiles < 0) return FA2_ERR_UNSUPPORTED;
     if (a.causal)
         return a.lse ? launch_v<D, DT, true, true>(a, p, st) : launch_v<D, DT, true, false>(a, p, st);
@@ -1177,8 +1199,7 @@ fa2_status launch_fwd_mfma(const FwdArgs &a, fa2_dtype dt, hipStream_t st) {
 }
 
 size_t mfma_workspace_bytes(int B, int H, int Nq, int Nk, int D, int causal, int num_cus) {
-    (void)causal;
-    const Plan p = plan(B, H, Nq, Nk, D, num_cus);
+    const Plan p = plan(B, H, Nq, Nk, D, causal, num_cus);
     if (p.rows || p.chunks <= 1) return 0;
     if (p.chunks == 2) return PairLayout(p.n_tiles, kWaves * 32 * p.qg, D).bytes;
     return (size_t)B * H * Nq * p.chunks * (D + 3) * sizeof(float);

@@ -154,6 +154,17 @@ def test_workspace_size_plan():
     assert fa2.workspace_size(1, 8, 2500, 2500, 64, 1, f16) == pair(160, 64)
     assert fa2.workspace_size(1, 2, 1000, 300, 128, 0, bf16) == pair(16, 128)
     assert fa2.workspace_size(1, 2, 300, 300, 128, 1, f16) == pair(6, 128)
+    # ... also at shorter keys where the tiles fill at most an eighth of the
+    # slots (16 blocks or more), and at D = 64 at most half of them (32 blocks
+    # or more) when causal or when the halves lower the most tiles per CU
+    assert fa2.workspace_size(1, 8, 1024, 1024, 64, 0, f16) == pair(64, 64)
+    assert fa2.workspace_size(1, 8, 1024, 1024, 128, 1, bf16) == pair(64, 128)
+    assert fa2.workspace_size(2, 12, 2048, 2048, 64, 1, f16) == pair(384, 64)
+    assert fa2.workspace_size(2, 12, 2048, 2048, 64, 0, f16) == pair(384, 64)
+    assert fa2.workspace_size(2, 8, 2048, 2048, 64, 1, f16) == pair(256, 64)
+    assert fa2.workspace_size(2, 8, 2048, 2048, 64, 0, f16) == 0     # 256 tiles: one per CU either way
+    assert fa2.workspace_size(1, 12, 2048, 2048, 128, 0, f16) == 0   # D = 128 at half the slots
+    assert fa2.workspace_size(4, 12, 1024, 1024, 64, 0, f16) == 0    # 16 blocks at half the slots
     # D = 128 splits the same way, with D + 3 floats per row and chunk
     need128 = fa2.workspace_size(1, 2, 4096, 4096, 128, 1, f16)
     assert need128 > 0 and need128 % (2 * 4096 * 131 * 4) == 0

@@ -449,7 +449,9 @@ PAIR_SHAPES = [(1, 8, 1024, 2500, 64, False, None),  # 64 tiles over 40 key bloc
                                                      # holds no visible key for most rows
                (1, 2, 1000, 300, 128, False, None),  # few tiles at D = 128, five key blocks
                (1, 2, 300, 300, 128, True, None),
-               (4, 12, 1024, 4096, 64, False, [0, 23, 47])]  # B4 H12 1024 x 4096: three heads
+               (4, 12, 1024, 4096, 64, False, [0, 23, 47]),  # B4 H12 1024 x 4096: three heads
+               (1, 8, 1024, 1024, 64, True, None),   # 64 tiles: an eighth of the slots, 16 blocks
+               (2, 12, 2048, 2048, 64, True, [0, 11, 23])]  # causal, half of the slots
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])

@@ -50,11 +50,14 @@ def _check_replays(name, refill, call):
 
 @pytest.mark.parametrize("dt,D,causal,N,H", [("f16", 64, True, 1024, 2), ("bf16", 128, False, 700, 2),
                                              ("f32", 64, False, 4096, 1), ("f32", 128, True, 512, 2),
-                                             ("bf16", 64, True, 4096, 2)])
+                                             ("bf16", 64, True, 4096, 2), ("f16", 64, True, 1024, 8)])
 def test_forward_graph(dt, D, causal, N, H):
-    """attn_fwd with the LSE; the f16 causal case (16 query tiles of 128
-    rows) runs the 32-row keys-across-waves kernel, and the bf16 N4096 case
-    the key split across workgroups with its workspace and combine kernel."""
+    """attn_fwd with the LSE; the f16 causal case with two heads (16 query
+    tiles of 128 rows) runs the 32-row keys-across-waves kernel, the bf16
+    N4096 case the key split across workgroups with its workspace and combine
+    kernel, and the f16 case with eight heads (64 tiles) the split in two
+    merged in the kernel, whose handshake tag is drawn once, at capture, and
+    replayed."""
     import torch
     from gpu_util import torch_dtype
     B = 1
