@@ -720,6 +720,392 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
 
 
 // ---------------------------------------------------------------------------
+// The same forward (keys not split) on v_mfma_f32_16x16x32_{f16,bf16}, whose
+// 16-row tiles let a wave own QB blocks of 16 query rows.  With QB = 1 a
+// shape whose 32-row waves would fill at most half of the wave slots gets
+// twice the waves (16 rows each), with no split of the keys and no merge;
+// every wave still walks all of its rows' keys.  Per 32-key tile and wave,
+// with kb in {0, 1} the 16-key blocks, qb < QB the 16-query blocks and dc the
+// 32-wide chunks of D:
+//     S^T[kb][qb] = sum_dc K[16 keys of kb][32 d of dc] Q^T[32 d][16 queries of qb]
+//     O^T[db][qb] += V^T[16 d of db][32 keys] P^T[32 keys][16 queries of qb]
+// Register layouts (16x16x32 MFMA: A lane l holds row l%16, contraction
+// slots 8(l/16)..+7; B lane l column l%16, the same slots; accumulator lane l
+// register r holds row 4(l/16) + r, column l%16), with g = l/16, c = l%16:
+//   * S^T[kb][qb] register r: key 16kb + 4g + r, query 16qb + c.  A lane thus
+//     holds 8 scores of each of two queries; a query's 32 scores of the tile
+//     lie in the four lanes c, c+16, c+32, c+48.
+//   * P^T for query block qb is the B operand as it stands: contraction slot
+//     j of lane (g, c) is key 16(j/4) + 4g + j%4, i.e. registers (kb, r) =
+//     (j/4, j%4) of S^T[kb][qb], packed in pairs.
+//   * V^T[db] pairs the same slots: two transposed LDS reads, keys 4g..4g+3
+//     and 16+4g..16+4g+3, column 16db + c.
+//   * O^T[db][qb] register r: d = 16db + 4g + r, query 16qb + c.
+template <int DT>
+struct Mfma16T;
+template <>
+struct Mfma16T<1> {
+    static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                                      __builtin_bit_cast(half8, b), c, 0, 0, 0);
+    }
+};
+template <>
+struct Mfma16T<2> {
+    static __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+template <int D, int DT, bool CAUSAL, bool WLSE, int QB>
+__global__ __launch_bounds__(kWaves * 64, D == 64 ? 3 : 2) void fwd_mfma16_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, uint16_t *__restrict__ O, float *__restrict__ LSE,
+    int Nq, int Nk, float scale_log2, int n_qtiles, int n_tiles, int snake) {
+    static_assert(D == 64 || D == 128, "head dimension");
+    constexpr int kD = D;
+    constexpr int NDC = D / 32;                     // 32-wide contraction chunks of S^T
+    constexpr int NDB = D / 16;                     // 16-row blocks of O^T
+    constexpr int CPR = D / 8;                      // 16-byte chunks per LDS row
+    constexpr int UPL = kBC * CPR / (kWaves * 64);  // 16-byte DMA units per lane per block
+    constexpr int ROWS = kWaves * 16 * QB;          // query rows per workgroup
+    // LDS: as in fwd_mfma_kernel (K buffers one 32-key tile ahead of V's).
+    __shared__ __attribute__((aligned(16))) uint16_t sK0[kBC * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t sK1[kBC * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t sV0[kBC * kD];
+    __shared__ __attribute__((aligned(16))) uint16_t sV1[kBC * kD];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+
+    // Tile order: as in fwd_mfma_kernel.
+    int bh, qt;
+    if (CAUSAL && snake > 0) {
+        const int per_xcd = n_tiles >> 3, hpx = per_xcd / n_qtiles;
+        const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+        const int r = pos / snake, i = pos - r * snake;
+        const int cnt = min(snake, per_xcd - r * snake);
+        const int k = r * snake + ((r & 1) ? cnt - 1 - i : i);
+        qt = n_qtiles - 1 - k / hpx;
+        bh = xcd * hpx + k % hpx;
+    } else if (CAUSAL) {
+        const int n_bh = n_tiles / n_qtiles;
+        const int rank = (int)blockIdx.x / n_bh;
+        qt = n_qtiles - 1 - rank;
+        bh = (int)blockIdx.x - rank * n_bh;
+    } else {
+        int wg = blockIdx.x;
+        if ((n_tiles & 7) == 0) wg = (wg & 7) * (n_tiles >> 3) + (wg >> 3);
+        bh = wg / n_qtiles;
+        qt = wg - bh * n_qtiles;
+    }
+    const int q0 = qt * ROWS;
+    const int qw = q0 + wave * 16 * QB;  // first row of this wave
+
+    const uint16_t *Qh = Q + (size_t)bh * Nq * kD;
+    const uint16_t *Kh = K + (size_t)bh * Nk * kD;
+    const uint16_t *Vh = V + (size_t)bh * Nk * kD;
+    const auto rq = make_rsrc(Qh, (uint32_t)Nq * kD * 2);
+    const auto rk = make_rsrc(Kh, (uint32_t)Nk * kD * 2);
+    const auto rv = make_rsrc(Vh, (uint32_t)Nk * kD * 2);
+
+    // Scale sign and zero: as in fwd_mfma_kernel.
+    const uint32_t qflip = scale_log2 < 0.f ? 0x80008000u : 0u;
+    const uint32_t qkeep = scale_log2 == 0.f ? 0u : 0xFFFFFFFFu;
+    scale_log2 = scale_log2 == 0.f ? 1.f : fabsf(scale_log2);
+
+    // B operand of S^T for query block qb, chunk dc: slot j of lane (g, c) is
+    // Q[qw + 16qb + c][32dc + 8g + j].
+    u32x4 qf[QB][NDC];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc)
+            qf[qb][dc] = load16(rq, (uint32_t)(((qw + 16 * qb + c) * kD + 32 * dc + 8 * g) * 2));
+
+    const int kend = CAUSAL ? min(Nk, q0 + ROWS) : Nk;
+    const int nblk = (kend + kBC - 1) / kBC;
+    const int t_last = CAUSAL ? min((kend + 31) / 32 - 1, (qw + 16 * QB - 1) / 32) : 2 * nblk - 1;
+
+    if (Nk % kBC != 0) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < UPL; ++i) {
+            reinterpret_cast<u32x4 *>(sV0)[tid + 256 * i] = z;
+            reinterpret_cast<u32x4 *>(sV1)[tid + 256 * i] = z;
+        }
+        __syncthreads();
+    }
+
+    // Block copies: as in fwd_mfma_kernel.
+    auto dma = [&](const __amdgpu_buffer_rsrc_t &r, uint16_t *dst, int k0, bool r_is_k) {
+#pragma unroll
+        for (int i = 0; i < UPL; ++i) {
+            const int unit = (UPL * wave + i) * 64 + lane;
+            const int row = unit / CPR;
+            const int ch = (unit % CPR) ^ (r_is_k ? kswz<D>(row) : vswz<D>(row));
+            const int key = k0 + row;
+            const uint32_t off = key < 0 ? 0xFFFFFFF0u : (uint32_t)((key * kD + ch * 8) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (UPL * wave + i) * 512), 16,
+                                                     off, 0, 0, 0);
+        }
+    };
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    auto dma_at = [&](const uint16_t *X, uint16_t *dst, int k0, bool r_is_k) {
+        const int kb = k0 < Nk ? k0 : Nk;
+        const auto r = make_rsrc(X + (size_t)kb * kD, (uint32_t)(Nk - kb) * kD * 2);
+#pragma unroll
+        for (int i = 0; i < UPL; ++i) {
+            const int unit = (UPL * wave + i) * 64 + lane;
+            const int row = unit / CPR;
+            const int ch = (unit % CPR) ^ (r_is_k ? kswz<D>(row) : vswz<D>(row));
+            const uint32_t off = (uint32_t)((row * kD + ch * 8) * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + (UPL * wave_s + i) * 512), 16,
+                                                     off, 0, 0, 0);
+        }
+    };
+
+    // LDS offsets relative to a tile's first row (both halves of a 64-row
+    // buffer share the swizzle).  K: row 16kb + c, chunk 4dc + g.  V (the
+    // transposed read, 4 rows x 16 columns per 16-lane group): lane c points at
+    // row 4g + c/4 + 16u and columns 16db + 4(c%4) .. +3, and receives column
+    // 16db + c of those 4 rows.
+    int kofs[2][NDC], vofs[NDB][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) {
+            const int key = 16 * kb + c;
+            kofs[kb][dc] = key * kD + (((4 * dc + g) ^ kswz<D>(key)) << 3);
+        }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int key = 4 * g + (c >> 2) + 16 * u;
+            const int d = 16 * db + 4 * (c & 3);
+            vofs[db][u] = key * kD + (((d >> 3) ^ vswz<D>(key)) << 3) + (d & 7);
+        }
+
+    float m[QB], mu[QB], l[QB], lt[QB];  // per query block: max used for the exponentials
+                                         // (base 2), that max or 0 while the row has none,
+                                         // this lane's shares of the denominators (f32 P,
+                                         // rounded P)
+    // Wave-uniform: some lane's row has no max yet (every tile then takes the max).
+    bool no_max = true;
+    const uint32_t ones = DT == 1 ? 0x3C003C00u : 0x3F803F80u;
+    f32x4 oacc[NDB][QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m[qb] = -INFINITY;
+        mu[qb] = 0.f;
+        l[qb] = lt[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // One 32-key tile t; scur holds S^T of tile t ([kb][qb]), kn points at the
+    // LDS rows of tile t+1's keys and vt at those of tile t's values.  With
+    // NEXT the scores of tile t+1 go to snext, issued among this tile's
+    // exponentials.
+    auto tile = [&](const int t, const uint16_t *kn, const uint16_t *vt, f32x4 (*scur)[QB],
+                    f32x4 (*snext)[QB], auto next_tag) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+        const int k0 = 32 * t;
+        u32x4 kf[2][NDC];
+        if constexpr (NEXT) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int dc = 0; dc < NDC; ++dc)
+                    kf[kb][dc] = *reinterpret_cast<const u32x4 *>(&kn[kofs[kb][dc]]);
+        }
+        u32x4 vf[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vofs[db][0]));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + vofs[db][1]));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+            const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+            vf[db] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+        }
+
+        const bool need_mask = (k0 + 32 > Nk) || (CAUSAL && k0 + 31 > qw);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = k0 + 16 * kb + 4 * g + r;
+                        bool ok = key < Nk;
+                        if (CAUSAL) ok = ok && key <= qw + 16 * qb + c;
+                        if (!ok) scur[kb][qb][r] = -INFINITY;
+                    }
+        }
+        // P of query block qb, packed as its B operand (pk[qb][2kb + r/2]),
+        // with the row sums of the rounded P (lp) and of the f32 P (ps).
+        u32x4 pk[QB];
+        float ps[QB], lp[QB];
+        auto exps = [&](int qb, float m_use, bool with_next) __attribute__((always_inline)) {
+            ps[qb] = 0.f;
+            float lp0 = 0.f, lp1 = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const float x0 = __builtin_fmaf(scur[kb][qb][2 * h2], scale_log2, -m_use);
+                    const float x1 = __builtin_fmaf(scur[kb][qb][2 * h2 + 1], scale_log2, -m_use);
+                    const float p0 = exp2f_fast(x0);
+                    const float p1 = exp2f_fast(x1);
+                    const uint32_t w = pack2<DT>(p0, p1);
+                    pk[qb][2 * kb + h2] = w;
+                    if constexpr (WLSE) ps[qb] += p0 + p1;
+                    if (h2 == 0) lp0 = dot2<DT>(w, ones, lp0); else lp1 = dot2<DT>(w, ones, lp1);
+                    if constexpr (NEXT) {
+                        // the next tile's score block (kb, qb), among this block's exponentials
+                        if (with_next && h2 == 0) {
+#pragma unroll
+                            for (int dc = 0; dc < NDC; ++dc)
+                                snext[kb][qb] = Mfma16T<DT>::mma(kf[kb][dc], qf[qb][dc],
+                                                               dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : snext[kb][qb]);
+                        }
+                    }
+                }
+            lp[qb] = lp0 + lp1;
+        };
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) exps(qb, mu[qb], true);
+        // Conditional rescaling: as in fwd_mfma_kernel, one test for all query
+        // blocks (taking the max of a block whose P stayed under the cap is
+        // also exact), the row max taken over the four lanes of each query.
+        float lpmax = lp[0];
+#pragma unroll
+        for (int qb = 1; qb < QB; ++qb) lpmax = fmaxf(lpmax, lp[qb]);
+        if (no_max || __builtin_amdgcn_ballot_w64(lpmax > kLazyCap) != 0) {
+            bool none = false;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, scur[kb][qb][r]);
+                mx = max_xor32(max_xor16(mx)) * scale_log2;
+                const float m_new = fmaxf(m[qb], mx);
+                mu[qb] = m_new == -INFINITY ? 0.f : m_new;
+                const float corr = exp2f_fast(m[qb] - mu[qb]);
+                l[qb] *= corr;
+                lt[qb] *= corr;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) oacc[db][qb] *= corr;
+                m[qb] = m_new;
+                none = none || m_new == -INFINITY;
+                exps(qb, mu[qb], false);
+            }
+            no_max = __builtin_amdgcn_ballot_w64(none) != 0;
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db][qb] = Mfma16T<DT>::mma(vf[db], pk[qb], oacc[db][qb]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            lt[qb] += lp[qb];
+            if constexpr (WLSE) l[qb] += ps[qb];
+        }
+    };
+
+    auto run_tile = [&](const int t, const uint16_t *kn, const uint16_t *vt, f32x4 (*scur)[QB],
+                        f32x4 (*snext)[QB]) {
+        if constexpr (CAUSAL) {
+            if (t > t_last) return;
+            if (t + 1 <= t_last)
+                tile(t, kn, vt, scur, snext, std::true_type{});
+            else
+                tile(t, kn, vt, scur, snext, std::false_type{});
+        } else {
+            tile(t, kn, vt, scur, snext, std::true_type{});
+        }
+    };
+
+    auto block = [&](int b, const uint16_t *kc, uint16_t *kd, const uint16_t *vc, uint16_t *vd,
+                     f32x4 (*sa)[QB], f32x4 (*sb)[QB]) {
+        if (b + 1 < nblk) {
+            dma_at(Vh, vd, (b + 1) * kBC, false);
+            dma_at(Kh, kd, (b + 1) * kBC + 32, true);
+        }
+        run_tile(2 * b, kc, vc, sa, sb);
+        run_tile(2 * b + 1, kc + 32 * kD, vc + 32 * kD, sb, sa);
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+    };
+
+    if (nblk > 0) {
+        dma(rv, sV0, 0, false);
+        dma(rk, sK0, 32, true);
+        dma(rk, sK1, -32, true);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int dc = 0; dc < NDC; ++dc) qf[qb][dc] = (qf[qb][dc] ^ qflip) & qkeep;
+        f32x4 sa[2][QB], sb[2][QB];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int dc = 0; dc < NDC; ++dc) {
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(&sK1[32 * kD + kofs[kb][dc]]);
+                    sa[kb][qb] = Mfma16T<DT>::mma(a, qf[qb][dc], dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sa[kb][qb]);
+                }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+
+        for (int b = 0; b < nblk; b += 2) {
+            block(b, sK0, sK1, sV0, sV1, sa, sb);
+            if (b + 1 < nblk) block(b + 1, sK1, sK0, sV1, sV0, sa, sb);
+        }
+    }
+
+    // Each query's sums over its four lanes.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        lt[qb] += __shfl_xor(lt[qb], 16);
+        lt[qb] += __shfl_xor(lt[qb], 32);
+        if constexpr (WLSE) {
+            l[qb] += __shfl_xor(l[qb], 16);
+            l[qb] += __shfl_xor(l[qb], 32);
+        }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int myq = qw + 16 * qb + c;
+        if (myq < Nq) {
+            const float inv = 1.f / lt[qb];
+            uint16_t *orow = O + ((size_t)bh * Nq + myq) * kD;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                u32x2 w;
+                w[0] = pack2<DT>(oacc[db][qb][0] * inv, oacc[db][qb][1] * inv);
+                w[1] = pack2<DT>(oacc[db][qb][2] * inv, oacc[db][qb][3] * inv);
+                *reinterpret_cast<u32x2 *>(orow + 16 * db + 4 * g) = w;
+            }
+            if constexpr (WLSE) {
+                if (g == 0) LSE[(size_t)bh * Nq + myq] = (m[qb] + log2f_fast(l[qb])) * kLn2;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Few query rows: one workgroup per 32 query rows whose W waves each walk a
 // contiguous slice of the keys, then merge their W partial states through LDS
 // with the (m, l) monoid ("Flash Attention", section Deriving the online
@@ -1007,6 +1393,7 @@ constexpr int kRowsWaves = 8;
 struct Plan {
     int qg, n_qtiles, n_tiles, chunks;
     bool rows;  // few query tiles: fwd_rows_kernel (32-row workgroups, keys split across waves)
+    bool q16;   // 16-row waves: fwd_mfma16_kernel with one query block per wave (64-row tiles)
 };
 
 #ifndef FA2_MFMA_SPLIT_WGS
@@ -1035,6 +1422,9 @@ struct Plan {
 #ifndef FA2_MFMA_PAIR
 #define FA2_MFMA_PAIR 1  // more shapes split in two, merged in the kernel (0: off)
 #endif
+#ifndef FA2_MFMA_Q16
+#define FA2_MFMA_Q16 1  // 16-row waves on 16x16x32 MFMAs when 32-row waves fill at most half the slots
+#endif
 #ifndef FA2_MFMA_SPLIT_LONG_HALF
 #define FA2_MFMA_SPLIT_LONG_HALF 64  // ... or at most half of the slots and at least this many
                                       // blocks (0: never)
@@ -1057,6 +1447,7 @@ Plan plan(int B, int H, int Nq, int Nk, int D, int causal, int num_cus) {
     p.n_tiles = nt > 0x7FFFFFFF ? -1 : (int)nt;
     p.chunks = 1;
     p.rows = false;
+    p.q16 = false;
     const long long nblk = (Nk + kBC - 1) / kBC;
     const long long nt32 = (long long)((Nq + 31) / 32) * B * H;
     if (FA2_MFMA_ROWS && D == 64 && nt > 0 && nt * FA2_MFMA_SPLIT_BELOW <= num_cus &&
@@ -1098,6 +1489,24 @@ Plan plan(int B, int H, int Nq, int Nk, int D, int causal, int num_cus) {
         if ((8 * nt <= slots && nblk >= 16) ||
             (D == 64 && 2 * nt <= slots && nblk >= 32 && (causal || fewer)))
             p.chunks = 2;
+    }
+    if (FA2_MFMA_Q16 && D == 64 && p.qg == 1 && p.chunks == 1 && !p.rows && nt > 0 &&
+        2 * nt <= 3LL * num_cus && (causal || 8 * nt >= 9LL * num_cus)) {
+        // The 128-row tiles fill at most half of the wave slots: 64-row tiles
+        // of 16-row waves (fwd_mfma16_kernel, QB = 1) give twice the waves --
+        // when causal (the shorter tiles also even out the mask's uneven
+        // lengths), or when the doubled tiles fill at least three quarters of
+        // the slots.  Measured (f16 unless noted): B4 H12 N1024 21.9 -> 20.2 us
+        // (bf16 21.2 -> 19.6), causal 18.9 -> 16.1, B2 H12 N1024 causal 17.8 ->
+        // 15.3, B8 H12 N512 causal 12.1 -> 10.1; against B4 H12 N512 9.38 ->
+        // 9.48, B2 H12 N1000 bf16 14.3 -> 14.6, B2 H8 and B1 H16 N2048 24.8 ->
+        // 25.4 with 16-row waves (half or two thirds of the slots filled).
+        const long long nt64 = (long long)((Nq + 63) / 64) * B * H;
+        if (nt64 <= 0x7FFFFFFF) {
+            p.q16 = true;
+            p.n_qtiles = (Nq + 63) / 64;
+            p.n_tiles = (int)nt64;
+        }
     }
     return p;
 }
@@ -1154,6 +1563,12 @@ fa2_status launch_q(const FwdArgs &a, const Plan &p, hipStream_t st) {
         return launch_combine_rows(o_part, m_part, l_part, a.o, a.lse, (size_t)a.B * a.H * a.Nq, D,
                                    p.chunks, DT == 1 ? FA2_F16 : FA2_BF16, st,
                                    WLSE ? l2_part : nullptr);
+    }
+    if constexpr (QG == 1 && D == 64) {
+        if (p.q16)
+            return launch(fwd_mfma16_kernel<D, DT, CAUSAL, WLSE, 1>, dim3((unsigned)p.n_tiles),
+                          dim3(kWaves * 64), st, q, k, v, (uint16_t *)a.o, a.lse, a.Nq, a.Nk, sl2,
+                          p.n_qtiles, p.n_tiles, snake_cus<D, QG>(a, p));
     }
     return launch(fwd_mfma_kernel<D, DT, CAUSAL, WLSE, false, QG>, dim3((unsigned)p.n_tiles),
                   dim3(kWaves * 64), st, q, k, v, (uint16_t *)a.o, a.lse, (float *)nullptr,

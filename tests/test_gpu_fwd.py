@@ -441,6 +441,40 @@ def test_long_keys_split_at_half_the_slots(dt):
         assert_close("half-slot split %s LSE" % tag, download_f64(lse)[:, heads], rl, LSE_TOL)
 
 
+# f16/bf16 shapes that run 16-row waves on 16x16x32 MFMAs (64-row tiles, keys
+# not split): at D = 64 the 128-row tiles fill at most half of the wave slots
+# (three per CU) and the shape is causal or its 64-row tiles fill at least three
+# quarters of the slots (256 CUs).  (B, H, Nq, Nk, causal, scale)
+Q16_SHAPES = [(4, 12, 1024, 1024, False, 0.125),  # the B4 H12 N1024 workload's shape
+              (4, 12, 1024, 1024, True, 0.125),
+              (2, 12, 1024, 1024, True, 0.5),      # 384 tiles: half of the slots, causal
+              (8, 12, 512, 512, True, 0.125),
+              (4, 12, 1000, 1000, False, 0.125),   # ragged rows and keys
+              (3, 16, 1000, 1000, True, 0.5),      # ragged, causal, peaky softmax
+              (4, 12, 1024, 700, False, 0.125)]    # Nq != Nk, ragged keys
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", Q16_SHAPES, ids=lambda s: "x".join(map(str, s[:5])))
+def test_mfma16_row_waves(shape, dt):
+    """Every row against the oracle, with and without LSE (the same O bit for
+    bit), and the same bits on a second call."""
+    import torch
+    B, H, Nq, Nk, causal, scale = shape
+    code = fa2.FA2_F16 if dt == "f16" else fa2.FA2_BF16
+    assert fa2.workspace_size(B, H, Nq, Nk, 64, causal, code) == 0, "the shape splits its keys"
+    q, k, v = seeded(B, H, Nq, Nk, 64, dt, 17)
+    o, lse = run_fwd(q, k, v, dt, scale, causal)
+    q64, k64, v64 = (inputs.to_f64(x, dt) for x in (q, k, v))
+    ro, rl = oracle.attn(q64, k64, v64, scale, causal)
+    wabs = oracle.attn(q64, k64, np.abs(v64), scale, causal)[0]
+    tag = "16-row waves %s %s" % (dt, "x".join(map(str, shape)))
+    assert_close(tag + " O", o, ro, edge_tol(dt, ro, o, wabs))
+    assert_close(tag + " LSE", lse, rl, LSE_TOL)
+    o2, lse2 = run_fwd(q, k, v, dt, scale, causal)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2), "not deterministic"
+
+
 # f16/bf16 shapes whose keys are split in exactly two chunks, the pair's
 # states merged in the kernel: (B, H, Nq, Nk, D, causal, flat heads checked
 # against the oracle, None for all)
