@@ -1,6 +1,6 @@
 // fwd_mfma.hip -- exact attention forward, f16 / bf16 in and out, D = 64 or
-// 128, on gfx950 matrix cores (v_mfma_f32_32x32x16_{f16,bf16}), f32 softmax
-// state.
+// 128, on gfx950 matrix cores (v_mfma_f32_32x32x16_{f16,bf16}; shapes with
+// few tiles also v_mfma_f32_16x16x32, in 16-row waves), f32 softmax state.
 //
 // Method: the FlashAttention-2 forward ("Flash Attention" (aarnphm.xyz),
 // sections Deriving the online softmax and FlashAttention 2; "06: Fused
