@@ -733,8 +733,8 @@ __global__ __launch_bounds__(kWaves * 64, QG == 1 && D == 64 ? 3 : 2) void fwd_m
 // slots 8(l/16)..+7; B lane l column l%16, the same slots; accumulator lane l
 // register r holds row 4(l/16) + r, column l%16), with g = l/16, c = l%16:
 //   * S^T[kb][qb] register r: key 16kb + 4g + r, query 16qb + c.  A lane thus
-//     holds 8 scores of each of two queries; a query's 32 scores of the tile
-//     lie in the four lanes c, c+16, c+32, c+48.
+//     holds 8 scores of each of its QB queries; a query's 32 scores of the
+//     tile lie in the four lanes c, c+16, c+32, c+48.
 //   * P^T for query block qb is the B operand as it stands: contraction slot
 //     j of lane (g, c) is key 16(j/4) + 4g + j%4, i.e. registers (kb, r) =
 //     (j/4, j%4) of S^T[kb][qb], packed in pairs.
