@@ -1425,6 +1425,9 @@ struct Plan {
 #ifndef FA2_MFMA_Q16
 #define FA2_MFMA_Q16 1  // 16-row waves on 16x16x32 MFMAs when 32-row waves fill at most half the slots
 #endif
+#ifndef FA2_MFMA_Q16_D128
+#define FA2_MFMA_Q16_D128 1  // the same at D = 128 (two workgroups per CU), causal shapes
+#endif
 #ifndef FA2_MFMA_SPLIT_LONG_HALF
 #define FA2_MFMA_SPLIT_LONG_HALF 64  // ... or at most half of the slots and at least this many
                                       // blocks (0: never)
@@ -1490,8 +1493,9 @@ Plan plan(int B, int H, int Nq, int Nk, int D, int causal, int num_cus) {
             (D == 64 && 2 * nt <= slots && nblk >= 32 && (causal || fewer)))
             p.chunks = 2;
     }
-    if (FA2_MFMA_Q16 && D == 64 && p.qg == 1 && p.chunks == 1 && !p.rows && nt > 0 &&
-        2 * nt <= 3LL * num_cus && (causal || 8 * nt >= 9LL * num_cus)) {
+    const bool q16_fit = D == 64 ? 2 * nt <= 3LL * num_cus && (causal || 8 * nt >= 9LL * num_cus)
+                                 : FA2_MFMA_Q16_D128 && causal && nt <= num_cus;
+    if (FA2_MFMA_Q16 && p.qg == 1 && p.chunks == 1 && !p.rows && nt > 0 && q16_fit) {
         // The 128-row tiles fill at most half of the wave slots: 64-row tiles
         // of 16-row waves (fwd_mfma16_kernel, QB = 1) give twice the waves --
         // when causal (the shorter tiles also even out the mask's uneven
@@ -1501,6 +1505,10 @@ Plan plan(int B, int H, int Nq, int Nk, int D, int causal, int num_cus) {
         // 15.3, B8 H12 N512 causal 12.1 -> 10.1; against B4 H12 N512 9.38 ->
         // 9.48, B2 H12 N1000 bf16 14.3 -> 14.6, B2 H8 and B1 H16 N2048 24.8 ->
         // 25.4 with 16-row waves (half or two thirds of the slots filled).
+        // At D = 128 (two workgroups per CU) only when causal: B2 H12 N1024
+        // causal f16 24.8 -> 23.3 us, B4 H12 N512 causal bf16 15.5 -> 14.4,
+        // B1 H16 N2048 causal 43.4 -> 41.3; unmasked they lose: B2 H12 N1024
+        // 23.4 -> 26.9, B1 H12 N2048 37.3 -> 47.3.
         const long long nt64 = (long long)((Nq + 63) / 64) * B * H;
         if (nt64 <= 0x7FFFFFFF) {
             p.q16 = true;
@@ -1564,7 +1572,7 @@ fa2_status launch_q(const FwdArgs &a, const Plan &p, hipStream_t st) {
                                    p.chunks, DT == 1 ? FA2_F16 : FA2_BF16, st,
                                    WLSE ? l2_part : nullptr);
     }
-    if constexpr (QG == 1 && D == 64) {
+    if constexpr (QG == 1 && (D == 64 || FA2_MFMA_Q16_D128)) {
         if (p.q16)
             return launch(fwd_mfma16_kernel<D, DT, CAUSAL, WLSE, 1>, dim3((unsigned)p.n_tiles),
                           dim3(kWaves * 64), st, q, k, v, (uint16_t *)a.o, a.lse, a.Nq, a.Nk, sl2,

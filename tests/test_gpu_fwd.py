@@ -445,25 +445,30 @@ def test_long_keys_split_at_half_the_slots(dt):
 # not split): at D = 64 the 128-row tiles fill at most half of the wave slots
 # (three per CU) and the shape is causal or its 64-row tiles fill at least three
 # quarters of the slots (256 CUs).  (B, H, Nq, Nk, causal, scale)
-Q16_SHAPES = [(4, 12, 1024, 1024, False, 0.125),  # the B4 H12 N1024 workload's shape
-              (4, 12, 1024, 1024, True, 0.125),
-              (2, 12, 1024, 1024, True, 0.5),      # 384 tiles: half of the slots, causal
-              (8, 12, 512, 512, True, 0.125),
-              (4, 12, 1000, 1000, False, 0.125),   # ragged rows and keys
-              (3, 16, 1000, 1000, True, 0.5),      # ragged, causal, peaky softmax
-              (4, 12, 1024, 700, False, 0.125)]    # Nq != Nk, ragged keys
+Q16_SHAPES = [(4, 12, 1024, 1024, 64, False, 0.125),  # the B4 H12 N1024 workload's shape
+              (4, 12, 1024, 1024, 64, True, 0.125),
+              (2, 12, 1024, 1024, 64, True, 0.5),      # 384 tiles: half of the slots, causal
+              (8, 12, 512, 512, 64, True, 0.125),
+              (4, 12, 1000, 1000, 64, False, 0.125),   # ragged rows and keys
+              (3, 16, 1000, 1000, 64, True, 0.5),      # ragged, causal, peaky softmax
+              (4, 12, 1024, 700, 64, False, 0.125),    # Nq != Nk, ragged keys
+              # D = 128, causal, 128-row tiles filling at most half of the slots
+              (2, 12, 1024, 1024, 128, True, 0.125),   # 192 tiles
+              (4, 12, 512, 512, 128, True, 0.5),
+              (1, 16, 2048, 2048, 128, True, 0.088),   # 256 tiles
+              (2, 7, 1000, 1000, 128, True, 0.125)]    # ragged: 112 tiles, 16 key blocks
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
-@pytest.mark.parametrize("shape", Q16_SHAPES, ids=lambda s: "x".join(map(str, s[:5])))
+@pytest.mark.parametrize("shape", Q16_SHAPES, ids=lambda s: "x".join(map(str, s[:6])))
 def test_mfma16_row_waves(shape, dt):
     """Every row against the oracle, with and without LSE (the same O bit for
     bit), and the same bits on a second call."""
     import torch
-    B, H, Nq, Nk, causal, scale = shape
+    B, H, Nq, Nk, D, causal, scale = shape
     code = fa2.FA2_F16 if dt == "f16" else fa2.FA2_BF16
-    assert fa2.workspace_size(B, H, Nq, Nk, 64, causal, code) == 0, "the shape splits its keys"
-    q, k, v = seeded(B, H, Nq, Nk, 64, dt, 17)
+    assert fa2.workspace_size(B, H, Nq, Nk, D, causal, code) == 0, "the shape splits its keys"
+    q, k, v = seeded(B, H, Nq, Nk, D, dt, 17)
     o, lse = run_fwd(q, k, v, dt, scale, causal)
     q64, k64, v64 = (inputs.to_f64(x, dt) for x in (q, k, v))
     ro, rl = oracle.attn(q64, k64, v64, scale, causal)
