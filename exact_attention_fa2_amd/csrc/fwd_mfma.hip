@@ -1493,8 +1493,8 @@ Plan plan(int B, int H, int Nq, int Nk, int D, int causal, int num_cus) {
             (D == 64 && 2 * nt <= slots && nblk >= 32 && (causal || fewer)))
             p.chunks = 2;
     }
-    const bool q16_fit = D == 64 ? 2 * nt <= 3LL * num_cus && (causal || 8 * nt >= 9LL * num_cus)
-                                 : FA2_MFMA_Q16_D128 && causal && nt <= num_cus;
+    const bool q16_fit = 2 * nt <= 3LL * num_cus &&
+                         (D == 64 ? causal || 8 * nt >= 9LL * num_cus : FA2_MFMA_Q16_D128 && causal);
     if (FA2_MFMA_Q16 && p.qg == 1 && p.chunks == 1 && !p.rows && nt > 0 && q16_fit) {
         // The 128-row tiles fill at most half of the wave slots: 64-row tiles
         // of 16-row waves (fwd_mfma16_kernel, QB = 1) give twice the waves --
@@ -1507,8 +1507,9 @@ Plan plan(int B, int H, int Nq, int Nk, int D, int causal, int num_cus) {
         // 25.4 with 16-row waves (half or two thirds of the slots filled).
         // At D = 128 (two workgroups per CU) only when causal: B2 H12 N1024
         // causal f16 24.8 -> 23.3 us, B4 H12 N512 causal bf16 15.5 -> 14.4,
-        // B1 H16 N2048 causal 43.4 -> 41.3; unmasked they lose: B2 H12 N1024
-        // 23.4 -> 26.9, B1 H12 N2048 37.3 -> 47.3.
+        // B1 H16 N2048 causal 43.4 -> 41.3, B4 H12 N1024 causal 29.5 -> 27.4
+        // (384 tiles); against B2 H16 N2048 causal 50.3 -> 54.2 (512 tiles)
+        // and, unmasked, B2 H12 N1024 23.4 -> 26.9, B1 H12 N2048 37.3 -> 47.3.
         const long long nt64 = (long long)((Nq + 63) / 64) * B * H;
         if (nt64 <= 0x7FFFFFFF) {
             p.q16 = true;

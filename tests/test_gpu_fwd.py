@@ -452,10 +452,11 @@ Q16_SHAPES = [(4, 12, 1024, 1024, 64, False, 0.125),  # the B4 H12 N1024 workloa
               (4, 12, 1000, 1000, 64, False, 0.125),   # ragged rows and keys
               (3, 16, 1000, 1000, 64, True, 0.5),      # ragged, causal, peaky softmax
               (4, 12, 1024, 700, 64, False, 0.125),    # Nq != Nk, ragged keys
-              # D = 128, causal, 128-row tiles filling at most half of the slots
+              # D = 128, causal, at most 1.5 128-row tiles per CU
               (2, 12, 1024, 1024, 128, True, 0.125),   # 192 tiles
               (4, 12, 512, 512, 128, True, 0.5),
               (1, 16, 2048, 2048, 128, True, 0.088),   # 256 tiles
+              (4, 12, 1024, 1024, 128, True, 0.125),   # 384 tiles: 1.5 per CU
               (2, 7, 1000, 1000, 128, True, 0.125)]    # ragged: 112 tiles, 16 key blocks
 
 
