@@ -1423,7 +1423,7 @@ struct Plan {
 #define FA2_MFMA_PAIR 1  // more shapes split in two, merged in the kernel (0: off)
 #endif
 #ifndef FA2_MFMA_Q16
-#define FA2_MFMA_Q16 1  // 16-row waves on 16x16x32 MFMAs when 32-row waves fill at most half the slots
+#define FA2_MFMA_Q16 1  // 16-row waves on 16x16x32 MFMAs when 32-row waves fill at most half the slots (D = 64)
 #endif
 #ifndef FA2_MFMA_Q16_D128
 #define FA2_MFMA_Q16_D128 1  // the same at D = 128 (two workgroups per CU), causal shapes
