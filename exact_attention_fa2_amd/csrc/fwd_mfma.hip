@@ -1388,7 +1388,10 @@ __global__ __launch_bounds__(W * 64, 1) void fwd_rows_kernel(
 // Waves of fwd_rows_kernel (two per SIMD), each on its own slice of the keys.
 // The kernel runs at D = 64: at D = 128 its ring of operands does not fit two
 // waves' registers, and the key split across workgroups measured faster there.
-constexpr int kRowsWaves = 8;
+#ifndef FA2_ROWS_WAVES
+#define FA2_ROWS_WAVES 8  // waves of fwd_rows_kernel (splitting the keys of 32 query rows)
+#endif
+constexpr int kRowsWaves = FA2_ROWS_WAVES;
 
 struct Plan {
     int qg, n_qtiles, n_tiles, chunks;
